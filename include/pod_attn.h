@@ -1,0 +1,238 @@
+/*
+ * pod_attn.h - C ABI of the MI355X (gfx950) Prefill-On-Decode attention library.
+ *
+ * One pod_run() call is one kernel launch that computes paged-KV-cache attention
+ * for two roles at once: a (chunked, causal) prefill batch and a decode batch.
+ * It writes O and a base-2 LSE per (query token, qo head) for each role.
+ *
+ * Sources, FlashInfer pages:
+ *   [POD]   www.dpshk.com/news/5405057  (PODWithPagedKVCacheWrapper /
+ *           BatchPODWithPagedKVCacheWrapper article)
+ *   [TOUR]  www.gsyq.cn/news/442943     (FlashInfer README tour)
+ *   [CUDNN] www.gsyq.cn/news/452757     (flashinfer.cudnn backend article)
+ *
+ * Lifecycle: plan once, run many ([POD] "plan/run 生命周期"). pod_plan() takes
+ * host copies of the length arrays only and turns them into a work list that is
+ * copied into the caller's int workspace; pod_run() may then be called once per
+ * layer with different q / KV / output pointers of the same shapes. All policy
+ * (causal, window, scale, sinks on/off) is fixed at plan time, as the batch
+ * wrapper does ([POD] "BatchPOD 的 run 差异").
+ *
+ * Ownership: the caller allocates and owns every device buffer (queries, KV
+ * pools, page indices, outputs, LSE, sinks and both workspaces). The library
+ * keeps host plan state and two small pinned staging buffers; pod_run() never
+ * allocates device memory and never synchronises the host.
+ *
+ * Errors: every entry point returns 0 on success or one of the POD_ERR_* codes;
+ * pod_last_error() returns a message for the calling thread's last failure. On
+ * an error nothing is enqueued on the stream.
+ */
+#ifndef POD_ATTN_H
+#define POD_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  POD_OK = 0,
+  POD_ERR_INVALID = 1,      /* bad shapes, page tables, ranges or null pointers */
+  POD_ERR_UNSUPPORTED = 2,  /* head_dim != 128, unknown dtype, group size > 128 */
+  POD_ERR_NOT_PLANNED = 3,  /* pod_run before pod_plan, or args that contradict the plan */
+  POD_ERR_WORKSPACE = 4,    /* a workspace is smaller than the plan needs */
+  POD_ERR_HIP = 5           /* a HIP runtime call failed (message in pod_last_error) */
+};
+
+enum { POD_DTYPE_F16 = 0, POD_DTYPE_BF16 = 1 };
+
+/* Item order policies for the fused grid (see pod_plan_desc.order). */
+enum { POD_ORDER_INTERLEAVE = 0, POD_ORDER_PREFILL_FIRST = 1, POD_ORDER_DECODE_FIRST = 2 };
+
+/*
+ * One role of the POD call ([POD] "批量 POD" plan inputs: qo_indptr, kv_indptr,
+ * last_page_len per side). All arrays are HOST memory, int32, read during
+ * pod_plan() only.
+ *   batch         number of requests; 0 leaves the role empty.
+ *   qo_indptr     [batch+1] query-token offsets; qo_indptr[0] == 0, non-decreasing.
+ *                 Rows of request b are q[qo_indptr[b] .. qo_indptr[b+1]).
+ *   kv_indptr     [batch+1] offsets into kv_indices; kv_indptr[0] == 0, strictly
+ *                 increasing (every request holds at least one page).
+ *   last_page_len [batch] 1 <= last_page_len[b] <= page_size. The request's KV
+ *                 length is (pages - 1) * page_size + last_page_len ([POD]
+ *                 "plan 内部做了什么", get_seq_lens).
+ *   causal        bottom-right causal mask: row i of a request with q_len rows
+ *                 and kv_len keys sees keys 0 .. kv_len - q_len + i ([CUDNN]
+ *                 "Decode 能力矩阵与参数", q_len_per_req). Requires kv_len >= q_len.
+ *   window_left   -1 = off; else row i also drops keys before p_i - window_left,
+ *                 p_i = kv_len - q_len + i, so window_left keys strictly before the
+ *                 diagonal plus the diagonal remain ([CUDNN] window alignment note).
+ *   sm_scale      softmax scale; <= 0 selects 1/sqrt(head_dim) ([POD] "Prefill 侧参数").
+ */
+typedef struct pod_role_desc {
+  int32_t batch;
+  const int32_t* qo_indptr;
+  const int32_t* kv_indptr;
+  const int32_t* last_page_len;
+  int32_t causal;
+  int32_t window_left;
+  float sm_scale;
+} pod_role_desc;
+
+/*
+ * Plan description.
+ *   num_qo_heads, num_kv_heads  num_qo_heads must be a multiple of num_kv_heads;
+ *                 qo head h reads kv head h / (num_qo_heads / num_kv_heads) (GQA,
+ *                 [POD] "plan/run 生命周期"). Group size must be <= 128.
+ *   head_dim      must be 128.
+ *   page_size     tokens per page, >= 1.
+ *   dtype         POD_DTYPE_F16 or POD_DTYPE_BF16; q, K/V and O share it. LSE is fp32.
+ *   has_sinks     1: pod_run takes a per-qo-head fp32 sink logit, an extra softmax
+ *                 term with a zero value row ([CUDNN] "Decode 能力矩阵与参数", sinks).
+ *   num_cus       compute units to plan for; 0 asks the device (pod_plan) or uses 256
+ *                 (pod_plan_compute / pod_workspace_bytes).
+ *   decode_chunk  keys per split of a decode request: 0 = planner's choice,
+ *                 -1 = never split, else rounded up to a multiple of 64.
+ *   order         POD_ORDER_* policy for how prefill and decode items share the grid.
+ */
+typedef struct pod_plan_desc {
+  pod_role_desc prefill;
+  pod_role_desc decode;
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t dtype;
+  int32_t has_sinks;
+  int32_t num_cus;
+  int32_t decode_chunk;
+  int32_t order;
+} pod_plan_desc;
+
+/*
+ * Device buffers of one role for pod_run(). Strides are in elements.
+ *   q        [rows, num_qo_heads, 128]: element (t, h, d) at t*q_stride_tok +
+ *            h*q_stride_head + d (head_dim innermost and dense).
+ *   k_cache, v_cache  paged pools. Element (page, slot, kv_head, d) at
+ *            page*kv_stride_page + slot*kv_stride_tok + kv_head*kv_stride_head + d,
+ *            for K and V alike. The combined NHD cache [P, 2, page_size, H_kv, 128]
+ *            of [POD] "批量 POD" is k_cache = base, v_cache = base + page_size*H_kv*128,
+ *            kv_stride_page = 2*page_size*H_kv*128, kv_stride_tok = H_kv*128,
+ *            kv_stride_head = 128. HND pools only change the strides.
+ *   kv_indices  [kv_indptr[batch]] int32 physical page ids, or NULL for identity
+ *            (logical page n is physical page n).
+ *   out      [rows, num_qo_heads, 128] in dtype, element (t, h, d) at
+ *            t*out_stride_tok + h*out_stride_head + d.
+ *   lse      [rows, num_qo_heads] fp32 base-2 LSE (sink excluded), dense; or NULL.
+ */
+typedef struct pod_role_args {
+  const void* q;
+  int64_t q_stride_tok;
+  int64_t q_stride_head;
+  const void* k_cache;
+  const void* v_cache;
+  int64_t kv_stride_page;
+  int64_t kv_stride_tok;
+  int64_t kv_stride_head;
+  const int32_t* kv_indices;
+  void* out;
+  int64_t out_stride_tok;
+  int64_t out_stride_head;
+  float* lse;
+} pod_role_args;
+
+/* sinks: device fp32 [num_qo_heads]; required iff the plan had has_sinks. */
+typedef struct pod_run_args {
+  pod_role_args prefill;
+  pod_role_args decode;
+  const float* sinks;
+} pod_run_args;
+
+/* Counts of what a plan holds (filled by pod_plan_compute / pod_plan_stats). */
+typedef struct pod_plan_info {
+  int32_t n_items;          /* work items (workgroups with work) */
+  int32_t n_prefill_items;
+  int32_t n_decode_items;
+  int32_t n_groups;         /* split (request, kv head) units that need the LSE merge */
+  int32_t n_slots;          /* partial-state slots in the float workspace */
+  int32_t grid;             /* workgroups launched (>= n_items; holes are idle) */
+  int32_t decode_chunk;     /* keys per decode split actually used */
+  int32_t image_ints;       /* int32 words of the work-list image */
+  int64_t float_ws_bytes;   /* float workspace the plan needs */
+  int64_t int_ws_bytes;     /* int workspace the plan needs */
+} pod_plan_info;
+
+typedef struct pod_ctx* pod_ctx_t;
+
+/*
+ * Create a context bound to HIP device `device`. float_ws and int_ws are
+ * caller-owned device buffers on that device (128 MB for the float workspace is
+ * the pages' default, [POD] "使用建议与已知限制"). The context stores the
+ * pointers; it does not take ownership.
+ */
+int pod_create(pod_ctx_t* out, int device, void* float_ws, size_t float_ws_bytes,
+               void* int_ws, size_t int_ws_bytes);
+
+/* Release the context's host state and staging buffers. NULL is accepted. */
+int pod_destroy(pod_ctx_t ctx);
+
+/*
+ * Validate `desc`, build the work list on the host and enqueue its copy into the
+ * int workspace on `stream` (a hipStream_t; NULL = default stream). The copy is
+ * stream-ordered, so a pod_run() on the same stream sees it. Not to be called
+ * during stream capture. Replaces any previous plan of this context.
+ */
+int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream);
+
+/* Info about the context's current plan. */
+int pod_plan_stats(pod_ctx_t ctx, pod_plan_info* info);
+
+/*
+ * Enqueue the fused attention launch on `stream`: exactly one kernel launch
+ * (none if the plan holds no work). Buffers must match the plan's shapes and
+ * dtype. Asynchronous; allocates nothing; leaves the workspace counters at zero
+ * when the launch completes, so runs can be repeated without a re-plan.
+ */
+int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* pod_last_error(void);
+
+/* Workspace sizes `desc` needs (host only; no device access). */
+int pod_workspace_bytes(const pod_plan_desc* desc, size_t* float_ws_bytes,
+                        size_t* int_ws_bytes);
+
+/*
+ * The planner alone, on the host: validate `desc` and write the work-list image
+ * (the exact int32 words pod_plan copies to the device) into `image`, which has
+ * room for `image_cap` words. `info` (optional) receives the counts. Returns
+ * POD_ERR_WORKSPACE with info->image_ints set if `image` is too small. No device
+ * access, so it runs without a GPU. Image layout: see pod_image_layout below.
+ */
+int pod_plan_compute(const pod_plan_desc* desc, int32_t* image, size_t image_cap,
+                     pod_plan_info* info);
+
+/*
+ * Work-list image layout (int32 words), for inspection by tools and tests.
+ *   header[POD_HDR_WORDS]: [0] magic POD_IMAGE_MAGIC, [1] n_items, [2] grid,
+ *     [3] n_reqs, [4] n_groups, [5] reqs_off, [6] items_off, [7] groups_off,
+ *     [8] counters_off, [9] n_slots, [10] slot_floats, [11] decode_chunk.
+ *   reqs[n_reqs][4]: {qo_start, qo_len, kv_len, page_start} per request, prefill
+ *     requests first, then decode requests.
+ *   items[grid][8]: {flags, req, kv_head, tok0, ntok, kv_begin, kv_end, group}; slot b
+ *     is the item of workgroup b. flags bit 0: role (0 prefill, 1 decode); bit 1:
+ *     kind (0 = query tile of up to 128 rows, 1 = key chunk of all q_len*group
+ *     rows, <= 32); bits 8..: split index; flags == -1 marks an idle slot.
+ *     group == -1: the item writes its output directly.
+ *   groups[n_groups][4]: {n_splits, first_slot, req, kv_head}.
+ *   counters[n_groups]: arrival counters, zero in the image.
+ */
+enum { POD_HDR_WORDS = 16, POD_IMAGE_MAGIC = 0x504f4431 };
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POD_ATTN_H */

@@ -1,0 +1,335 @@
+// Host planner: request lengths -> one work list for the fused POD grid.
+//
+// It follows what the POD article (www.dpshk.com/news/5405057) says plan() does
+// ("plan 内部做了什么", "Batch 版本 plan 的 colocated-CTA 调度细节"): read the
+// host copies of the length arrays, derive each request's KV length from its
+// page count and last_page_len, split decode KV into chunks (split-KV), and
+// decide how prefill and decode work share the device. Our version emits one
+// list of workgroup items for both roles instead of two kernel plans, and
+// places items on the MI355X's accelerator dies explicitly.
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "pod_internal.h"
+
+namespace pod {
+
+namespace {
+
+struct Item {
+  int32_t w[kItemWords];
+  double cost;
+  int xcd;
+};
+
+struct Req {
+  int role;
+  int b;
+  int32_t qo_start, qo_len, kv_len, page_start;
+};
+
+int fail(std::string* err, int code, const std::string& msg) {
+  if (err) *err = msg;
+  return code;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Relative cost estimates used only to order and place items. A query tile is
+// MFMA work proportional to padded rows x keys; a key chunk is HBM traffic
+// proportional to keys (K and V rows of one kv head). The constants put both
+// in microseconds per CU at a nominal fraction of MI355X peak.
+double tile_cost(int64_t keys) { return 128.0 * 4.0 * kHeadDim * (double)keys / 4.9e12 * 1e6; }
+double chunk_cost(int64_t keys) { return 2.0 * kHeadDim * 2.0 * (double)keys / 31.0e9 * 1e6; }
+
+int validate_role(const pod_role_desc& r, const char* name, int page_size, std::string* err) {
+  char buf[256];
+  if (r.batch < 0) {
+    snprintf(buf, sizeof buf, "%s.batch must be >= 0", name);
+    return fail(err, POD_ERR_INVALID, buf);
+  }
+  if (r.batch == 0) return POD_OK;
+  if (!r.qo_indptr || !r.kv_indptr || !r.last_page_len) {
+    snprintf(buf, sizeof buf, "%s: qo_indptr, kv_indptr and last_page_len are required", name);
+    return fail(err, POD_ERR_INVALID, buf);
+  }
+  if (r.qo_indptr[0] != 0 || r.kv_indptr[0] != 0) {
+    snprintf(buf, sizeof buf, "%s: qo_indptr[0] and kv_indptr[0] must be 0", name);
+    return fail(err, POD_ERR_INVALID, buf);
+  }
+  if (r.window_left < -1) {
+    snprintf(buf, sizeof buf, "%s.window_left must be -1 or >= 0", name);
+    return fail(err, POD_ERR_INVALID, buf);
+  }
+  for (int b = 0; b < r.batch; ++b) {
+    int64_t q0 = r.qo_indptr[b], q1 = r.qo_indptr[b + 1];
+    int64_t p0 = r.kv_indptr[b], p1 = r.kv_indptr[b + 1];
+    if (q1 < q0) {
+      snprintf(buf, sizeof buf, "%s: qo_indptr decreases at request %d", name, b);
+      return fail(err, POD_ERR_INVALID, buf);
+    }
+    if (p1 <= p0) {
+      snprintf(buf, sizeof buf, "%s: request %d holds no page (kv_indptr must increase)", name, b);
+      return fail(err, POD_ERR_INVALID, buf);
+    }
+    int32_t lpl = r.last_page_len[b];
+    if (lpl < 1 || lpl > page_size) {
+      snprintf(buf, sizeof buf, "%s: last_page_len[%d] = %d outside [1, page_size=%d]", name, b,
+               lpl, page_size);
+      return fail(err, POD_ERR_INVALID, buf);
+    }
+    int64_t kv_len = (p1 - p0 - 1) * (int64_t)page_size + lpl;
+    if (kv_len > INT32_MAX / 2) {
+      snprintf(buf, sizeof buf, "%s: request %d kv_len too large", name, b);
+      return fail(err, POD_ERR_INVALID, buf);
+    }
+    if (r.causal && kv_len < q1 - q0) {
+      snprintf(buf, sizeof buf, "%s: causal request %d has kv_len %lld < q_len %lld", name, b,
+               (long long)kv_len, (long long)(q1 - q0));
+      return fail(err, POD_ERR_INVALID, buf);
+    }
+  }
+  return POD_OK;
+}
+
+}  // namespace
+
+int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_info& info,
+                 std::string* err) {
+  info = pod_plan_info{};
+  if (d.num_qo_heads <= 0 || d.num_kv_heads <= 0)
+    return fail(err, POD_ERR_INVALID, "num_qo_heads and num_kv_heads must be positive");
+  if (d.num_qo_heads % d.num_kv_heads)
+    return fail(err, POD_ERR_INVALID, "num_qo_heads must be a multiple of num_kv_heads");
+  if (d.head_dim != kHeadDim) return fail(err, POD_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (d.page_size < 1) return fail(err, POD_ERR_INVALID, "page_size must be >= 1");
+  if (d.dtype != POD_DTYPE_F16 && d.dtype != POD_DTYPE_BF16)
+    return fail(err, POD_ERR_UNSUPPORTED, "dtype must be POD_DTYPE_F16 or POD_DTYPE_BF16");
+  if (d.order < 0 || d.order > 2) return fail(err, POD_ERR_INVALID, "unknown order policy");
+  const int g = d.num_qo_heads / d.num_kv_heads;
+  if (g > kTileRows) return fail(err, POD_ERR_UNSUPPORTED, "group size above 128 is not supported");
+  int rc = validate_role(d.prefill, "prefill", d.page_size, err);
+  if (rc) return rc;
+  rc = validate_role(d.decode, "decode", d.page_size, err);
+  if (rc) return rc;
+  const int num_cus = d.num_cus > 0 ? d.num_cus : 256;
+  const int H = d.num_kv_heads;
+
+  // per-request table: prefill requests first, then decode requests
+  std::vector<Req> reqs;
+  const pod_role_desc* roles[2] = {&d.prefill, &d.decode};
+  for (int role = 0; role < 2; ++role) {
+    const pod_role_desc& r = *roles[role];
+    for (int b = 0; b < r.batch; ++b) {
+      Req q;
+      q.role = role;
+      q.b = b;
+      q.qo_start = r.qo_indptr[b];
+      q.qo_len = r.qo_indptr[b + 1] - r.qo_indptr[b];
+      q.kv_len = (r.kv_indptr[b + 1] - r.kv_indptr[b] - 1) * d.page_size + r.last_page_len[b];
+      q.page_start = r.kv_indptr[b];
+      reqs.push_back(q);
+    }
+  }
+
+  // key range a request's rows need as a whole: [lo, kv_len)
+  auto chunk_lo = [&](const Req& q) -> int64_t {
+    const pod_role_desc& r = *roles[q.role];
+    int64_t p0 = (int64_t)q.kv_len - q.qo_len;
+    return r.window_left >= 0 ? std::max<int64_t>(0, p0 - r.window_left) : 0;
+  };
+  auto is_chunk = [&](const Req& q) { return (int64_t)q.qo_len * g <= kChunkRows; };
+
+  // decode split size: enough key-chunk items for ~4 per CU, at least 256 keys each
+  int64_t chunk_keys_total = 0;
+  for (const Req& q : reqs)
+    if (q.qo_len > 0 && is_chunk(q)) chunk_keys_total += (int64_t)H * (q.kv_len - chunk_lo(q));
+  int64_t C;
+  if (d.decode_chunk < 0) {
+    C = INT32_MAX;
+  } else if (d.decode_chunk > 0) {
+    C = round_up(d.decode_chunk, 64);
+  } else {
+    int64_t target = 4LL * num_cus;
+    C = std::max<int64_t>(256, round_up((chunk_keys_total + target - 1) / std::max<int64_t>(target, 1), 64));
+  }
+
+  std::vector<Item> items;
+  std::vector<int32_t> groups;  // n_groups x 4
+  int32_t n_slots = 0;
+  for (size_t ri = 0; ri < reqs.size(); ++ri) {
+    const Req& q = reqs[ri];
+    const pod_role_desc& r = *roles[q.role];
+    if (q.qo_len == 0) continue;
+    if (is_chunk(q)) {
+      int64_t lo = chunk_lo(q), hi = q.kv_len;
+      int64_t n = hi - lo;
+      int64_t splits = (n + C - 1) / C;
+      for (int kvh = 0; kvh < H; ++kvh) {
+        int32_t grp = -1;
+        if (splits > 1) {
+          grp = (int32_t)(groups.size() / kGroupWords);
+          groups.push_back((int32_t)splits);
+          groups.push_back(n_slots);
+          groups.push_back((int32_t)ri);
+          groups.push_back(kvh);
+          n_slots += (int32_t)splits;
+        }
+        for (int64_t s = 0; s < splits; ++s) {
+          Item it;
+          int64_t b0 = lo + s * C, b1 = std::min<int64_t>(hi, b0 + C);
+          it.w[0] = q.role | kFlagChunk | (int32_t)(s << kSplitShift);
+          it.w[1] = (int32_t)ri;
+          it.w[2] = kvh;
+          it.w[3] = 0;
+          it.w[4] = q.qo_len;
+          it.w[5] = (int32_t)b0;
+          it.w[6] = (int32_t)b1;
+          it.w[7] = grp;
+          it.cost = chunk_cost(b1 - b0);
+          it.xcd = -1;
+          items.push_back(it);
+        }
+      }
+    } else {
+      int T = std::max(1, kTileRows / g);
+      for (int t0 = 0; t0 < q.qo_len; t0 += T) {
+        int ntok = std::min(T, q.qo_len - t0);
+        int64_t pf = (int64_t)q.kv_len - q.qo_len + t0, pl = pf + ntok - 1;
+        int64_t hi = r.causal ? pl + 1 : q.kv_len;
+        int64_t lo = r.window_left >= 0 ? std::max<int64_t>(0, pf - r.window_left) : 0;
+        for (int kvh = 0; kvh < H; ++kvh) {
+          Item it;
+          it.w[0] = q.role;
+          it.w[1] = (int32_t)ri;
+          it.w[2] = kvh;
+          it.w[3] = t0;
+          it.w[4] = ntok;
+          it.w[5] = (int32_t)lo;
+          it.w[6] = (int32_t)hi;
+          it.w[7] = -1;
+          it.cost = tile_cost(hi - lo);
+          // tiles sharing one request's K/V for one kv head stay on one die (L2 reuse)
+          it.xcd = (int)((ri * (size_t)H + kvh) % kNumXcds);
+          items.push_back(it);
+        }
+      }
+    }
+  }
+
+  // Place items on dies. Tiles keep their die; key chunks go to the least loaded
+  // die, heaviest first (LPT).
+  std::vector<double> load(kNumXcds, 0.0);
+  std::vector<size_t> order(items.size());
+  for (size_t i = 0; i < items.size(); ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t a, size_t b) { return items[a].cost > items[b].cost; });
+  for (size_t i : order)
+    if (items[i].xcd >= 0) load[items[i].xcd] += items[i].cost;
+  for (size_t i : order) {
+    if (items[i].xcd >= 0) continue;
+    int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    items[i].xcd = best;
+    load[best] += items[i].cost;
+  }
+
+  // Per die: order by the policy. Each role's items run heaviest first;
+  // POD_ORDER_INTERLEAVE merges the two roles in proportion to their cost so
+  // both kinds are resident on every CU at once.
+  std::vector<std::vector<size_t>> per(kNumXcds);
+  for (size_t i : order) per[items[i].xcd].push_back(i);
+  size_t max_len = 0;
+  for (int x = 0; x < kNumXcds; ++x) {
+    std::vector<size_t> pre, dec;
+    for (size_t i : per[x]) ((items[i].w[0] & kFlagRole) ? dec : pre).push_back(i);
+    std::vector<size_t> out;
+    if (d.order == POD_ORDER_PREFILL_FIRST) {
+      out = pre;
+      out.insert(out.end(), dec.begin(), dec.end());
+    } else if (d.order == POD_ORDER_DECODE_FIRST) {
+      out = dec;
+      out.insert(out.end(), pre.begin(), pre.end());
+    } else {
+      double tp = 0, td = 0;
+      for (size_t i : pre) tp += items[i].cost;
+      for (size_t i : dec) td += items[i].cost;
+      double cp = 0, cd = 0;
+      size_t a = 0, b = 0;
+      while (a < pre.size() || b < dec.size()) {
+        bool take_pre;
+        if (a == pre.size()) take_pre = false;
+        else if (b == dec.size()) take_pre = true;
+        else take_pre = (cp / tp) <= (cd / td);
+        if (take_pre) { cp += items[pre[a]].cost; out.push_back(pre[a++]); }
+        else { cd += items[dec[b]].cost; out.push_back(dec[b++]); }
+      }
+    }
+    per[x] = out;
+    max_len = std::max(max_len, out.size());
+  }
+
+  const int64_t grid = (int64_t)max_len * kNumXcds;
+  const int n_groups = (int)(groups.size() / kGroupWords);
+  const int64_t reqs_off = POD_HDR_WORDS;
+  const int64_t items_off = reqs_off + (int64_t)reqs.size() * kReqWords;
+  const int64_t groups_off = items_off + grid * kItemWords;
+  const int64_t counters_off = groups_off + (int64_t)n_groups * kGroupWords;
+  const int64_t total = counters_off + n_groups;
+  if (grid > INT32_MAX / 2 || total > INT32_MAX / 2)
+    return fail(err, POD_ERR_UNSUPPORTED, "plan too large");
+
+  image.assign((size_t)total, 0);
+  int32_t* h = image.data();
+  h[0] = POD_IMAGE_MAGIC;
+  h[1] = (int32_t)items.size();
+  h[2] = (int32_t)grid;
+  h[3] = (int32_t)reqs.size();
+  h[4] = n_groups;
+  h[5] = (int32_t)reqs_off;
+  h[6] = (int32_t)items_off;
+  h[7] = (int32_t)groups_off;
+  h[8] = (int32_t)counters_off;
+  h[9] = n_slots;
+  h[10] = kSlotFloats;
+  h[11] = (int32_t)std::min<int64_t>(C, INT32_MAX);
+  for (size_t i = 0; i < reqs.size(); ++i) {
+    int32_t* p = h + reqs_off + i * kReqWords;
+    p[0] = reqs[i].qo_start;
+    p[1] = reqs[i].qo_len;
+    p[2] = reqs[i].kv_len;
+    p[3] = reqs[i].page_start;
+  }
+  for (int64_t s = 0; s < grid; ++s) {
+    int32_t* p = h + items_off + s * kItemWords;
+    for (int k = 0; k < kItemWords; ++k) p[k] = 0;
+    p[0] = -1;
+  }
+  int n_pre = 0, n_dec = 0;
+  for (int x = 0; x < kNumXcds; ++x) {
+    for (size_t k = 0; k < per[x].size(); ++k) {
+      const Item& it = items[per[x][k]];
+      int32_t* p = h + items_off + ((int64_t)k * kNumXcds + x) * kItemWords;
+      for (int j = 0; j < kItemWords; ++j) p[j] = it.w[j];
+      if (it.w[0] & kFlagRole) ++n_dec; else ++n_pre;
+    }
+  }
+  for (int i = 0; i < n_groups * kGroupWords; ++i) h[groups_off + i] = groups[i];
+
+  info.n_items = (int32_t)items.size();
+  info.n_prefill_items = n_pre;
+  info.n_decode_items = n_dec;
+  info.n_groups = n_groups;
+  info.n_slots = n_slots;
+  info.grid = (int32_t)grid;
+  info.decode_chunk = (int32_t)std::min<int64_t>(C, INT32_MAX);
+  info.image_ints = (int32_t)total;
+  info.float_ws_bytes = (int64_t)n_slots * kSlotFloats * 4;
+  info.int_ws_bytes = total * 4;
+  return POD_OK;
+}
+
+}  // namespace pod

@@ -1,0 +1,300 @@
+// C ABI of the POD attention library: validation, plan upload, launch.
+// The interface follows the plan-once / run-many wrappers of the POD article
+// (www.dpshk.com/news/5405057, "plan/run 生命周期", "BatchPOD 的 run 差异").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "pod_internal.h"
+
+namespace pod {
+int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_info& info,
+                 std::string* err);
+}
+
+namespace {
+
+thread_local std::string g_err;
+
+int set_err(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_err(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return POD_ERR_HIP;
+}
+
+struct RolePlan {
+  int32_t batch = 0;
+  int32_t rows = 0;
+  int32_t causal = 0;
+  int32_t window_left = -1;
+  float sm_scale = 0.f;
+};
+
+}  // namespace
+
+struct pod_ctx {
+  int device = 0;
+  void* float_ws = nullptr;
+  size_t float_bytes = 0;
+  void* int_ws = nullptr;
+  size_t int_bytes = 0;
+  int num_cus = 0;
+  bool planned = false;
+  RolePlan role[2];
+  int32_t num_qo_heads = 0, num_kv_heads = 0, page_size = 0, dtype = 0, has_sinks = 0;
+  pod_plan_info info{};
+  int32_t hdr[POD_HDR_WORDS] = {};
+  // two pinned staging buffers, reused once their last copy has completed
+  int32_t* staging[2] = {nullptr, nullptr};
+  size_t staging_cap[2] = {0, 0};
+  hipEvent_t staged[2] = {nullptr, nullptr};
+  bool staged_pending[2] = {false, false};
+  int next_staging = 0;
+};
+
+namespace {
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = true;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* pod_last_error(void) { return g_err.c_str(); }
+
+int pod_plan_compute(const pod_plan_desc* desc, int32_t* image, size_t image_cap,
+                     pod_plan_info* info) {
+  if (!desc) return set_err(POD_ERR_INVALID, "desc is NULL");
+  std::vector<int32_t> img;
+  pod_plan_info inf;
+  std::string err;
+  int rc = pod::plan_compute(*desc, img, inf, &err);
+  if (rc) return set_err(rc, err);
+  if (info) *info = inf;
+  if (img.size() > image_cap || (!image && !img.empty()))
+    return set_err(POD_ERR_WORKSPACE, "image buffer too small for the plan");
+  if (!img.empty()) memcpy(image, img.data(), img.size() * sizeof(int32_t));
+  g_err.clear();
+  return POD_OK;
+}
+
+int pod_workspace_bytes(const pod_plan_desc* desc, size_t* float_ws_bytes, size_t* int_ws_bytes) {
+  if (!desc) return set_err(POD_ERR_INVALID, "desc is NULL");
+  std::vector<int32_t> img;
+  pod_plan_info inf;
+  std::string err;
+  int rc = pod::plan_compute(*desc, img, inf, &err);
+  if (rc) return set_err(rc, err);
+  if (float_ws_bytes) *float_ws_bytes = (size_t)inf.float_ws_bytes;
+  if (int_ws_bytes) *int_ws_bytes = (size_t)inf.int_ws_bytes;
+  g_err.clear();
+  return POD_OK;
+}
+
+int pod_create(pod_ctx_t* out, int device, void* float_ws, size_t float_ws_bytes, void* int_ws,
+               size_t int_ws_bytes) {
+  if (!out) return set_err(POD_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  if (!int_ws || int_ws_bytes == 0) return set_err(POD_ERR_INVALID, "int workspace is required");
+  if (!float_ws && float_ws_bytes) return set_err(POD_ERR_INVALID, "float workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(float_ws) & 15) || (reinterpret_cast<uintptr_t>(int_ws) & 15))
+    return set_err(POD_ERR_INVALID, "workspaces must be 16-byte aligned");
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_err(e, "hipGetDeviceCount");
+  if (device < 0 || device >= ndev) return set_err(POD_ERR_INVALID, "device index out of range");
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_err(e, "hipDeviceGetAttribute");
+  pod_ctx* c = new pod_ctx();
+  c->device = device;
+  c->float_ws = float_ws;
+  c->float_bytes = float_ws_bytes;
+  c->int_ws = int_ws;
+  c->int_bytes = int_ws_bytes;
+  c->num_cus = cus;
+  *out = c;
+  g_err.clear();
+  return POD_OK;
+}
+
+int pod_destroy(pod_ctx_t ctx) {
+  if (!ctx) return POD_OK;
+  {
+    DeviceGuard dg(ctx->device);
+    for (int i = 0; i < 2; ++i) {
+      if (ctx->staged[i]) {
+        (void)hipEventSynchronize(ctx->staged[i]);
+        (void)hipEventDestroy(ctx->staged[i]);
+      }
+      if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
+    }
+  }
+  delete ctx;
+  return POD_OK;
+}
+
+int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
+  if (!ctx) return set_err(POD_ERR_INVALID, "ctx is NULL");
+  if (!desc) return set_err(POD_ERR_INVALID, "desc is NULL");
+  pod_plan_desc d = *desc;
+  if (d.num_cus <= 0) d.num_cus = ctx->num_cus;
+  std::vector<int32_t> img;
+  pod_plan_info inf;
+  std::string err;
+  int rc = pod::plan_compute(d, img, inf, &err);
+  if (rc) return set_err(rc, err);
+  if ((size_t)inf.int_ws_bytes > ctx->int_bytes)
+    return set_err(POD_ERR_WORKSPACE, "int workspace too small: need " +
+                                          std::to_string(inf.int_ws_bytes) + " bytes");
+  if ((size_t)inf.float_ws_bytes > ctx->float_bytes)
+    return set_err(POD_ERR_WORKSPACE, "float workspace too small: need " +
+                                          std::to_string(inf.float_ws_bytes) + " bytes");
+  DeviceGuard dg(ctx->device);
+  if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int k = ctx->next_staging;
+  hipError_t e;
+  if (ctx->staged_pending[k]) {
+    e = hipEventSynchronize(ctx->staged[k]);
+    if (e != hipSuccess) return hip_err(e, "hipEventSynchronize");
+    ctx->staged_pending[k] = false;
+  }
+  const size_t bytes = img.size() * sizeof(int32_t);
+  if (ctx->staging_cap[k] < bytes) {
+    if (ctx->staging[k]) (void)hipHostFree(ctx->staging[k]);
+    ctx->staging[k] = nullptr;
+    ctx->staging_cap[k] = 0;
+    size_t cap = bytes < 65536 ? 65536 : bytes * 2;
+    e = hipHostMalloc(reinterpret_cast<void**>(&ctx->staging[k]), cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_err(e, "hipHostMalloc");
+    ctx->staging_cap[k] = cap;
+  }
+  if (!ctx->staged[k]) {
+    e = hipEventCreateWithFlags(&ctx->staged[k], hipEventDisableTiming);
+    if (e != hipSuccess) return hip_err(e, "hipEventCreate");
+  }
+  memcpy(ctx->staging[k], img.data(), bytes);
+  e = hipMemcpyAsync(ctx->int_ws, ctx->staging[k], bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (work list)");
+  e = hipEventRecord(ctx->staged[k], s);
+  if (e != hipSuccess) return hip_err(e, "hipEventRecord");
+  ctx->staged_pending[k] = true;
+  ctx->next_staging = 1 - k;
+
+  const pod_role_desc* rd[2] = {&d.prefill, &d.decode};
+  for (int r = 0; r < 2; ++r) {
+    RolePlan& rp = ctx->role[r];
+    rp.batch = rd[r]->batch;
+    rp.rows = rd[r]->batch > 0 ? rd[r]->qo_indptr[rd[r]->batch] : 0;
+    rp.causal = rd[r]->causal ? 1 : 0;
+    rp.window_left = rd[r]->window_left;
+    rp.sm_scale = rd[r]->sm_scale > 0.f ? rd[r]->sm_scale : 1.0f / std::sqrt((float)d.head_dim);
+  }
+  ctx->num_qo_heads = d.num_qo_heads;
+  ctx->num_kv_heads = d.num_kv_heads;
+  ctx->page_size = d.page_size;
+  ctx->dtype = d.dtype;
+  ctx->has_sinks = d.has_sinks ? 1 : 0;
+  ctx->info = inf;
+  memcpy(ctx->hdr, img.data(), sizeof(ctx->hdr));
+  ctx->planned = true;
+  g_err.clear();
+  return POD_OK;
+}
+
+int pod_plan_stats(pod_ctx_t ctx, pod_plan_info* info) {
+  if (!ctx || !info) return set_err(POD_ERR_INVALID, "ctx and info are required");
+  if (!ctx->planned) return set_err(POD_ERR_NOT_PLANNED, "pod_plan has not been called");
+  *info = ctx->info;
+  return POD_OK;
+}
+
+int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
+  if (!ctx) return set_err(POD_ERR_INVALID, "ctx is NULL");
+  if (!args) return set_err(POD_ERR_INVALID, "args is NULL");
+  if (!ctx->planned) return set_err(POD_ERR_NOT_PLANNED, "pod_run called before pod_plan");
+  if (ctx->has_sinks && !args->sinks)
+    return set_err(POD_ERR_NOT_PLANNED, "plan has sinks: args->sinks is required");
+  if (!ctx->has_sinks && args->sinks)
+    return set_err(POD_ERR_NOT_PLANNED, "plan has no sinks: args->sinks must be NULL");
+  pod::Params p{};
+  const pod_role_args* ra[2] = {&args->prefill, &args->decode};
+  static const char* names[2] = {"prefill", "decode"};
+  for (int r = 0; r < 2; ++r) {
+    const RolePlan& rp = ctx->role[r];
+    const pod_role_args& a = *ra[r];
+    pod::RoleParams& o = p.role[r];
+    if (rp.rows > 0) {
+      if (!a.q || !a.k_cache || !a.v_cache || !a.out)
+        return set_err(POD_ERR_INVALID, std::string(names[r]) + ": q, k_cache, v_cache and out are required");
+      if (a.q_stride_tok <= 0 || a.q_stride_head <= 0 || a.kv_stride_page <= 0 ||
+          a.kv_stride_tok <= 0 || a.kv_stride_head <= 0 || a.out_stride_tok <= 0 ||
+          a.out_stride_head <= 0)
+        return set_err(POD_ERR_INVALID, std::string(names[r]) + ": strides must be positive");
+      const uintptr_t mis = reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k_cache) |
+                            reinterpret_cast<uintptr_t>(a.v_cache) | reinterpret_cast<uintptr_t>(a.out);
+      const int64_t smis = a.q_stride_tok | a.q_stride_head | a.kv_stride_page | a.kv_stride_tok |
+                           a.kv_stride_head | a.out_stride_tok | a.out_stride_head;
+      if ((mis & 15) || (smis & 7))
+        return set_err(POD_ERR_INVALID, std::string(names[r]) +
+                                             ": buffers must be 16-byte aligned and strides multiples of 8 elements");
+      if (a.lse && (reinterpret_cast<uintptr_t>(a.lse) & 3))
+        return set_err(POD_ERR_INVALID, std::string(names[r]) + ": lse must be 4-byte aligned");
+    }
+    o.q = a.q;
+    o.q_st = a.q_stride_tok;
+    o.q_sh = a.q_stride_head;
+    o.k = a.k_cache;
+    o.v = a.v_cache;
+    o.kv_sp = a.kv_stride_page;
+    o.kv_st = a.kv_stride_tok;
+    o.kv_sh = a.kv_stride_head;
+    o.indices = a.kv_indices;
+    o.out = a.out;
+    o.o_st = a.out_stride_tok;
+    o.o_sh = a.out_stride_head;
+    o.lse = a.lse;
+    o.scale_log2 = rp.sm_scale * 1.4426950408889634f;
+    o.causal = rp.causal;
+    o.window_left = rp.window_left;
+  }
+  int32_t* iws = reinterpret_cast<int32_t*>(ctx->int_ws);
+  p.reqs = iws + ctx->hdr[5];
+  p.items = iws + ctx->hdr[6];
+  p.groups = iws + ctx->hdr[7];
+  p.counters = iws + ctx->hdr[8];
+  p.partials = reinterpret_cast<float*>(ctx->float_ws);
+  p.sinks = args->sinks;
+  p.num_qo_heads = ctx->num_qo_heads;
+  p.num_kv_heads = ctx->num_kv_heads;
+  p.group_size = ctx->num_qo_heads / ctx->num_kv_heads;
+  p.page_size = ctx->page_size;
+  DeviceGuard dg(ctx->device);
+  if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
+  int e = pod::launch_pod_grid(p, ctx->dtype, ctx->info.grid, stream);
+  if (e != (int)hipSuccess) return hip_err((hipError_t)e, "pod grid launch");
+  g_err.clear();
+  return POD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal definitions shared by the host planner, the C ABI layer and the HIP
+// kernels of the POD attention library. Host-only code includes this file too,
+// so it names no HIP types.
+#pragma once
+
+#include <stdint.h>
+
+#include "pod_attn.h"
+
+namespace pod {
+
+constexpr int kHeadDim = 128;
+constexpr int kThreads = 256;          // 4 wave64 per workgroup
+constexpr int kTileRows = 128;         // rows of a query-tile item (4 waves x 32)
+constexpr int kChunkRows = 32;         // max rows of a key-chunk item (one MFMA column block)
+constexpr int kItemWords = 8;
+constexpr int kReqWords = 4;
+constexpr int kGroupWords = 4;
+constexpr int kNumXcds = 8;            // MI355X: 8 accelerator dies, 32 CUs each
+constexpr int kSlotFloats = kChunkRows * kHeadDim + kChunkRows;   // partial O + LSE
+
+// item flags
+constexpr int kFlagRole = 1;           // bit 0: 0 prefill, 1 decode
+constexpr int kFlagChunk = 2;          // bit 1: key-chunk item
+constexpr int kSplitShift = 8;
+
+struct RoleParams {
+  const void* q;
+  int64_t q_st, q_sh;
+  const void* k;
+  const void* v;
+  int64_t kv_sp, kv_st, kv_sh;
+  const int32_t* indices;   // nullptr = identity page table
+  void* out;
+  int64_t o_st, o_sh;
+  float* lse;               // nullptr = not requested
+  float scale_log2;         // sm_scale * log2(e)
+  int32_t causal;
+  int32_t window_left;
+};
+
+struct Params {
+  RoleParams role[2];
+  const int32_t* reqs;
+  const int32_t* items;
+  const int32_t* groups;
+  int32_t* counters;
+  float* partials;
+  const float* sinks;       // nullptr = no sinks
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t group_size;
+  int32_t page_size;
+};
+
+// Launch the fused grid on `stream` (a hipStream_t). Returns a hipError_t value.
+int launch_pod_grid(const Params& p, int dtype, int grid, void* stream);
+
+}  // namespace pod

@@ -1,0 +1,258 @@
+"""Python binding of the POD attention library: argument marshalling only.
+
+Mirrors the batch wrapper of the POD article (www.dpshk.com/news/5405057,
+"批量 POD" and "BatchPOD 的 run 差异"): plan() once from host length arrays,
+run() per layer, returning (out_p, out_d) or ((out_p, lse_p), (out_d, lse_d)).
+PyTorch supplies device memory and the current stream; every step of the
+attention itself runs in the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+import torch
+
+from . import _lib
+
+_DT = {torch.float16: _lib.POD_DTYPE_F16, torch.bfloat16: _lib.POD_DTYPE_BF16}
+KVCache = Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]
+
+
+def _host_i32(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach().to("cpu")
+        x = x.numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _dtype_code(dtype) -> int:
+    if isinstance(dtype, str):
+        dtype = {"f16": torch.float16, "float16": torch.float16, "half": torch.float16,
+                 "bf16": torch.bfloat16, "bfloat16": torch.bfloat16}[dtype]
+    if dtype not in _DT:
+        raise NotImplementedError(f"dtype {dtype} is not supported (float16 / bfloat16)")
+    return _DT[dtype]
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def kv_views(cache: KVCache, kv_layout: str):
+    """(k, v, page_stride, token_stride, head_stride) in elements for a paged cache.
+
+    cache: combined [P, 2, page_size, H_kv, D] (NHD) / [P, 2, H_kv, page_size, D]
+    (HND), or a (k_cache, v_cache) pair of [P, page_size, H_kv, D] / [P, H_kv,
+    page_size, D] tensors with equal strides.
+    """
+    if isinstance(cache, (tuple, list)):
+        k, v = cache
+    else:
+        if cache.dim() != 5 or cache.shape[1] != 2:
+            raise ValueError("combined paged cache must be [pages, 2, ...]")
+        k, v = cache[:, 0], cache[:, 1]
+    if k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("k and v caches must be 4-D with equal shapes and strides")
+    if k.stride(-1) != 1:
+        raise ValueError("head_dim must be the innermost, dense dimension")
+    if kv_layout == "NHD":
+        return k, v, k.stride(0), k.stride(1), k.stride(2)
+    if kv_layout == "HND":
+        return k, v, k.stride(0), k.stride(2), k.stride(1)
+    raise ValueError(f"unknown kv_layout {kv_layout!r}")
+
+
+class BatchPOD:
+    """Batch prefill + batch decode paged attention in one launch per run()."""
+
+    def __init__(self, float_workspace_buffer: torch.Tensor, kv_layout: str = "NHD",
+                 int_workspace_bytes: int = 8 << 20):
+        self._lib = _lib.load()
+        if not float_workspace_buffer.is_cuda:
+            raise ValueError("the float workspace must be a device tensor")
+        if kv_layout not in ("NHD", "HND"):
+            raise ValueError(f"unknown kv_layout {kv_layout!r}")
+        self.kv_layout = kv_layout
+        self.device = float_workspace_buffer.device
+        self._float_ws = float_workspace_buffer
+        self._int_ws = torch.zeros(int_workspace_bytes // 4, dtype=torch.int32, device=self.device)
+        ctx = ctypes.c_void_p()
+        _lib.check(self._lib.pod_create(
+            ctypes.byref(ctx), self.device.index if self.device.index is not None else 0,
+            ctypes.c_void_p(self._float_ws.data_ptr()), self._float_ws.numel() * self._float_ws.element_size(),
+            ctypes.c_void_p(self._int_ws.data_ptr()), self._int_ws.numel() * 4))
+        self._ctx = ctx
+        self._planned = None
+
+    def __del__(self):
+        ctx = getattr(self, "_ctx", None)
+        if ctx is not None and ctx.value:
+            self._lib.pod_destroy(ctx)
+            self._ctx = None
+
+    @staticmethod
+    def _role_desc(qo_indptr, kv_indptr, last_page_len, causal, window_left, sm_scale, keep):
+        if qo_indptr is None:
+            return _lib.PodRoleDesc(0, None, None, None, int(bool(causal)), int(window_left), 0.0)
+        qo = _host_i32(qo_indptr)
+        kv = _host_i32(kv_indptr)
+        lpl = _host_i32(last_page_len)
+        if qo.ndim != 1 or kv.shape != qo.shape or lpl.shape != (qo.shape[0] - 1,):
+            raise ValueError("indptr arrays must be [batch+1] and last_page_len [batch]")
+        keep.extend([qo, kv, lpl])
+        return _lib.PodRoleDesc(int(qo.shape[0] - 1), _ptr(qo), _ptr(kv), _ptr(lpl),
+                                int(bool(causal)), int(window_left),
+                                float(sm_scale) if sm_scale is not None else 0.0)
+
+    def plan(self, qo_indptr_p, kv_indptr_p, last_page_len_p,
+             qo_indptr_d, kv_indptr_d, last_page_len_d, *,
+             num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+             dtype=torch.bfloat16, causal_p: bool = True, causal_d: bool = True,
+             window_left_p: int = -1, window_left_d: int = -1,
+             sm_scale_p: Optional[float] = None, sm_scale_d: Optional[float] = None,
+             sinks: bool = False, decode_chunk: int = 0, order: int = 0, stream=None):
+        """Build and upload the work list. Either role may be None (empty)."""
+        keep = []
+        desc = _lib.PodPlanDesc(
+            self._role_desc(qo_indptr_p, kv_indptr_p, last_page_len_p, causal_p, window_left_p,
+                            sm_scale_p, keep),
+            self._role_desc(qo_indptr_d, kv_indptr_d, last_page_len_d, causal_d, window_left_d,
+                            sm_scale_d, keep),
+            int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size),
+            _dtype_code(dtype), int(bool(sinks)), 0, int(decode_chunk), int(order))
+        s = _stream_handle(self.device) if stream is None else ctypes.c_void_p(stream)
+        _lib.check(self._lib.pod_plan(self._ctx, ctypes.byref(desc), s))
+        nnz = []
+        rows = []
+        for qo, kv in ((qo_indptr_p, kv_indptr_p), (qo_indptr_d, kv_indptr_d)):
+            rows.append(int(_host_i32(qo)[-1]) if qo is not None else 0)
+            nnz.append(int(_host_i32(kv)[-1]) if kv is not None else 0)
+        self._planned = dict(
+            rows=tuple(rows), nnz=tuple(nnz),
+            num_qo_heads=int(num_qo_heads), num_kv_heads=int(num_kv_heads),
+            head_dim=int(head_dim), page_size=int(page_size), dtype=_dtype_code(dtype),
+            sinks=bool(sinks))
+        return self
+
+    def plan_info(self) -> dict:
+        info = _lib.PodPlanInfo()
+        _lib.check(self._lib.pod_plan_stats(self._ctx, ctypes.byref(info)))
+        return info.as_dict()
+
+    def _role_args(self, idx, q, cache, kv_indices, out, lse):
+        pl = self._planned
+        rows = pl["rows"][idx]
+        if rows == 0 or q is None:
+            return _lib.PodRoleArgs()
+        hq, d = pl["num_qo_heads"], pl["head_dim"]
+        if q.dim() != 3 or q.shape[0] != rows or q.shape[1] != hq or q.shape[2] != d:
+            raise ValueError(f"q must be [{rows}, {hq}, {d}], got {tuple(q.shape)}")
+        if _DT.get(q.dtype) != pl["dtype"]:
+            raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "q dtype differs from the planned dtype")
+        if q.stride(-1) != 1:
+            raise ValueError("q: head_dim must be dense")
+        k, v, sp, st, sh = kv_views(cache, self.kv_layout)
+        if k.dtype != q.dtype:
+            raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "kv dtype differs from q dtype")
+        ps = k.shape[1] if self.kv_layout == "NHD" else k.shape[2]
+        hk = k.shape[2] if self.kv_layout == "NHD" else k.shape[1]
+        if ps != pl["page_size"] or hk != pl["num_kv_heads"] or k.shape[3] != d:
+            raise ValueError("paged cache shape differs from the plan")
+        nnz = pl["nnz"][idx]
+        if kv_indices is not None:
+            if kv_indices.dtype != torch.int32 or not kv_indices.is_cuda or kv_indices.dim() != 1:
+                raise ValueError("kv_indices must be a 1-D int32 device tensor")
+            if kv_indices.numel() < nnz:
+                raise ValueError(f"kv_indices holds {kv_indices.numel()} pages, the plan needs {nnz}")
+        elif k.shape[0] < nnz:
+            raise ValueError(f"identity page table needs {nnz} pages, the cache has {k.shape[0]}")
+        return _lib.PodRoleArgs(
+            q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), v.data_ptr(), sp, st, sh,
+            kv_indices.data_ptr() if kv_indices is not None else None,
+            out.data_ptr(), out.stride(0), out.stride(1),
+            lse.data_ptr() if lse is not None else None)
+
+    def run(self, q_p, paged_kv_cache_p, kv_indices_p, q_d, paged_kv_cache_d, kv_indices_d, *,
+            sinks: Optional[torch.Tensor] = None, return_lse: bool = False,
+            out_p=None, out_d=None, lse_p=None, lse_d=None):
+        """One fused launch. Returns (out_p, out_d) or ((out_p, lse_p), (out_d, lse_d))."""
+        if self._planned is None:
+            raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "run() before plan()")
+        pl = self._planned
+        hq, d = pl["num_qo_heads"], pl["head_dim"]
+        outs, lses = [], []
+        for idx, q, o, l in ((0, q_p, out_p, lse_p), (1, q_d, out_d, lse_d)):
+            rows = pl["rows"][idx]
+            if q is None:
+                if rows:
+                    raise ValueError("a planned role needs its q tensor")
+                outs.append(None)
+                lses.append(None)
+                continue
+            if o is None:
+                o = torch.empty((rows, hq, d), dtype=q.dtype, device=q.device)
+            if l is None and return_lse:
+                l = torch.empty((rows, hq), dtype=torch.float32, device=q.device)
+            outs.append(o)
+            lses.append(l)
+        if pl["sinks"]:
+            if sinks is None or sinks.dtype != torch.float32 or sinks.numel() != hq or not sinks.is_cuda:
+                raise ValueError("plan has sinks: pass an fp32 [num_qo_heads] device tensor")
+        elif sinks is not None:
+            raise ValueError("plan has no sinks")
+        args = _lib.PodRunArgs(
+            self._role_args(0, q_p, paged_kv_cache_p, kv_indices_p, outs[0], lses[0]),
+            self._role_args(1, q_d, paged_kv_cache_d, kv_indices_d, outs[1], lses[1]),
+            sinks.data_ptr() if sinks is not None else None)
+        _lib.check(self._lib.pod_run(self._ctx, ctypes.byref(args), _stream_handle(self.device)))
+        if return_lse:
+            return (outs[0], lses[0]), (outs[1], lses[1])
+        return outs[0], outs[1]
+
+
+def single_decode_with_kv_cache(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                kv_layout: str = "NHD", window_left: int = -1,
+                                sm_scale: Optional[float] = None, return_lse: bool = False,
+                                workspace: Optional[torch.Tensor] = None):
+    """Single-request decode (README tour, "快速上手单请求 Decode 注意力").
+
+    q [num_qo_heads, head_dim]; k, v [kv_len, num_kv_heads, head_dim] (NHD) or
+    [num_kv_heads, kv_len, head_dim] (HND). Runs the fused grid with only the
+    decode role, treating the dense K/V as pages of one token.
+    """
+    if q.dim() != 2 or k.dim() != 3 or v.shape != k.shape:
+        raise ValueError("q must be [H_qo, D] and k, v [kv_len, H_kv, D]")
+    if kv_layout == "NHD":
+        kv_len, hk, d = k.shape
+        sp, sh = k.stride(0), k.stride(1)
+    elif kv_layout == "HND":
+        hk, kv_len, d = k.shape
+        sp, sh = k.stride(1), k.stride(0)
+    else:
+        raise ValueError(f"unknown kv_layout {kv_layout!r}")
+    if k.stride() != v.stride():
+        raise ValueError("k and v must share strides")
+    hq = q.shape[0]
+    if workspace is None:
+        workspace = torch.empty(16 << 20, dtype=torch.uint8, device=q.device)
+    w = BatchPOD(workspace, "NHD", int_workspace_bytes=1 << 20)
+    w.plan(None, None, None, [0, 1], [0, kv_len], [1],
+           num_qo_heads=hq, num_kv_heads=hk, head_dim=d, page_size=1, dtype=q.dtype,
+           causal_d=False, window_left_d=window_left, sm_scale_d=sm_scale)
+    # page_size 1 view: [kv_len, 1, H_kv, D] with the caller's strides
+    kp = torch.as_strided(k, (kv_len, 1, hk, d), (sp, sp, sh, 1))
+    vp = torch.as_strided(v, (kv_len, 1, hk, d), (sp, sp, sh, 1))
+    res = w.run(None, None, None, q.view(1, hq, d), (kp, vp), None, return_lse=return_lse)
+    if return_lse:
+        (_, _), (o, lse) = res
+        return o.view(hq, d), lse.view(hq)
+    return res[1].view(hq, d)

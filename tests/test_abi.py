@@ -1,0 +1,49 @@
+"""The C ABI library loads on a host without a GPU and exports every entry
+point include/pod_attn.h declares; error paths return their documented codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from serving_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "pod_attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(pod_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_entry_point():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_null_arguments_are_rejected():
+    lib = _lib.load()
+    assert lib.pod_plan_compute(None, None, 0, None) == _lib.POD_ERR_INVALID
+    assert b"NULL" in lib.pod_last_error()
+    assert lib.pod_workspace_bytes(None, None, None) == _lib.POD_ERR_INVALID
+    assert lib.pod_plan(None, None, None) == _lib.POD_ERR_INVALID
+    assert lib.pod_run(None, None, None) == _lib.POD_ERR_INVALID
+    assert lib.pod_destroy(None) == _lib.POD_OK
+    out = ctypes.c_void_p()
+    assert lib.pod_create(ctypes.byref(out), 0, None, 0, None, 0) == _lib.POD_ERR_INVALID
+    assert lib.pod_plan_stats(None, None) == _lib.POD_ERR_INVALID
+
+
+def test_error_codes_map_to_python_exceptions():
+    lib = _lib.load()
+    lib.pod_plan_compute(None, None, 0, None)
+    with pytest.raises(ValueError):
+        _lib.check(_lib.POD_ERR_INVALID)
+    with pytest.raises(NotImplementedError):
+        _lib.check(_lib.POD_ERR_UNSUPPORTED)
+    with pytest.raises(_lib.PodError):
+        _lib.check(_lib.POD_ERR_NOT_PLANNED)

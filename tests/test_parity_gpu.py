@@ -1,0 +1,234 @@
+"""GPU parity: the fused HIP launch (through the C ABI) against the fp64 oracle.
+
+Tolerances: max-abs error on O <= 5e-3 (fp16) / 2e-2 (bf16), on the base-2 LSE
+<= 1e-3. Small ragged cases compare every element; the five named workloads
+run at full size in the launch configuration the benchmark times and compare
+sampled rows (every row for the decode roles)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from serving_attention_amd import BatchPOD, single_decode_with_kv_cache, _lib
+from workloads import RoleSpec, WorkloadSpec, build, named_spec
+
+from gpu_helpers import TOL_LSE, TOL_O, assert_close, compare_role, log, oracle_request, plan_and_run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU on this host")
+
+
+def small_spec(name="small", dtype="bf16", ps=16, hqo=16, hkv=4, w=-1, sinks=False, dq=1,
+               p_q=(127, 33, 300), p_kv=(127, 60, 700), d_kv=(1, 16, 17, 100, 513, 1000, 2049),
+               seed=0, pool="shared", layout="NHD", spare=3):
+    return WorkloadSpec(
+        name=name,
+        prefill=RoleSpec(list(p_q), list(p_kv), causal=True, window_left=w) if p_q else None,
+        decode=RoleSpec([dq] * len(d_kv), [max(k, dq) for k in d_kv], causal=True, window_left=w) if d_kv else None,
+        num_qo_heads=hqo, num_kv_heads=hkv, page_size=ps, dtype=dtype, sinks=sinks, pool=pool,
+        shuffle_pages=True, spare_pages=spare, kv_layout=layout, meta_seed=100 + seed,
+        value_seed=200 + seed)
+
+
+def check_all(w, res, tag):
+    (op, lp), (od, ld) = res
+    if w.prefill is not None:
+        assert_close(w, compare_role(w, w.prefill, op, lp, tag=tag + "/prefill"), tag + "/prefill")
+    if w.decode is not None:
+        assert_close(w, compare_role(w, w.decode, od, ld, tag=tag + "/decode"), tag + "/decode")
+
+
+def test_tiny_key_chunk():
+    log("case: tiny key chunk (1 request, 1 token, 50 keys, f16)")
+    w = build(small_spec(dtype="f16", p_q=(), d_kv=(50,), hqo=8, hkv=2), device="cuda")
+    res, _ = plan_and_run(w, roles=("decode",))
+    check_all(w, res, "tiny-chunk")
+
+
+def test_tiny_query_tile():
+    log("case: tiny query tile (1 request, 70 tokens, bf16)")
+    w = build(small_spec(p_q=(70,), p_kv=(70,), d_kv=(), hqo=8, hkv=2), device="cuda")
+    res, _ = plan_and_run(w, roles=("prefill",))
+    check_all(w, res, "tiny-tile")
+
+
+GRID = [
+    dict(dtype="f16", ps=16, hqo=16, hkv=4),
+    dict(dtype="bf16", ps=1, hqo=16, hkv=4),
+    dict(dtype="bf16", ps=16, hqo=8, hkv=8),
+    dict(dtype="bf16", ps=16, hqo=32, hkv=4, w=37),
+    dict(dtype="f16", ps=5, hqo=16, hkv=2, sinks=True),
+    dict(dtype="bf16", ps=16, hqo=16, hkv=2, w=100, sinks=True, dq=4),
+    dict(dtype="bf16", ps=16, hqo=8, hkv=1, dq=3),
+    dict(dtype="f16", ps=16, hqo=64, hkv=2, dq=1),       # group 32: a full MFMA column block
+    dict(dtype="bf16", ps=16, hqo=64, hkv=1, dq=2),      # group 64: decode runs as query tiles
+    dict(dtype="bf16", ps=16, hqo=12, hkv=4, w=0),       # group 3, diagonal-only window
+    dict(dtype="bf16", ps=16, hqo=16, hkv=4, layout="HND"),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(GRID)), ids=[str(i) for i in range(len(GRID))])
+def test_small_grid(idx):
+    cfg = GRID[idx]
+    log(f"case: small grid {idx} {cfg}")
+    w = build(small_spec(seed=idx, **cfg), device="cuda")
+    res, _ = plan_and_run(w)
+    check_all(w, res, f"grid{cfg}")
+
+
+@pytest.mark.parametrize("chunk", [64, 128, 192, 256])
+def test_split_kv_merge(chunk):
+    log(f"case: split-KV merge, decode_chunk={chunk}")
+    w = build(small_spec(dq=2, w=300, sinks=True, d_kv=(1, 63, 64, 65, 700, 2000)), device="cuda")
+    res, pod = plan_and_run(w, decode_chunk=chunk)
+    assert pod.plan_info()["n_groups"] > 0
+    check_all(w, res, f"split{chunk}")
+
+
+def test_repeat_runs_are_bitwise_stable_and_counters_reset():
+    log("case: repeated runs with split-KV")
+    w = build(small_spec(dq=2, sinks=True), device="cuda")
+    res1, pod = plan_and_run(w, decode_chunk=64)
+    first = [t.clone() for pair in res1 for t in pair]
+    for _ in range(3):
+        res, _ = plan_and_run(w, decode_chunk=64, pod=pod)
+        again = [t for pair in res for t in pair]
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+    info = pod.plan_info()
+    h = pod._int_ws[:16].cpu().numpy()
+    counters = pod._int_ws[int(h[8]):int(h[8]) + info["n_groups"]].cpu().numpy()
+    assert np.all(counters == 0)
+
+
+def test_fused_equals_role_isolated():
+    log("case: fused vs role-isolated launches")
+    w = build(small_spec(dq=4, w=200, sinks=True), device="cuda")
+    fused, _ = plan_and_run(w)
+    pre, _ = plan_and_run(w, roles=("prefill",))
+    dec, _ = plan_and_run(w, roles=("decode",))
+    assert torch.equal(fused[0][0], pre[0][0]) and torch.equal(fused[0][1], pre[0][1])
+    assert torch.equal(fused[1][0], dec[1][0]) and torch.equal(fused[1][1], dec[1][1])
+
+
+def test_item_orders_agree():
+    log("case: item order policies")
+    w = build(small_spec(dq=1), device="cuda")
+    base, _ = plan_and_run(w, order=0)
+    for order in (1, 2):
+        res, _ = plan_and_run(w, order=order)
+        for a, b in zip(base, res):
+            assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_poisoned_unreferenced_slots_and_outputs():
+    log("case: NaN in unreferenced pool slots and in the output buffers")
+    spec = small_spec(dq=3, ps=16, pool="separate", spare=5, d_kv=(5, 17, 33, 300))
+    w = build(spec, device="cuda", poison=True)
+    res, _ = plan_and_run(w, poison_out=True, decode_chunk=64)
+    check_all(w, res, "poison")
+
+
+def test_empty_requests_and_single_key():
+    log("case: zero-length query requests and single-key requests")
+    w = build(small_spec(p_q=(0, 1, 5, 0), p_kv=(7, 1, 5, 3), d_kv=(1, 1, 2)), device="cuda")
+    res, _ = plan_and_run(w)
+    check_all(w, res, "empty")
+
+
+def test_single_decode_api_matches_oracle():
+    log("case: single_decode_with_kv_cache, README example shapes")
+    g = torch.Generator(device="cuda").manual_seed(1001)
+    q = torch.randn(32, 128, generator=g, device="cuda").half()
+    k = torch.randn(2048, 32, 128, generator=g, device="cuda").half()
+    v = torch.randn(2048, 32, 128, generator=g, device="cuda").half()
+    import oracle
+    ro, rl = oracle.attend_rows(q.float().cpu().numpy()[None], k.float().cpu().numpy(),
+                                v.float().cpu().numpy(), np.ones((1, 2048), bool), 128 ** -0.5)
+    for layout in ("NHD", "HND"):
+        kk = k if layout == "NHD" else k.transpose(0, 1).contiguous()
+        vv = v if layout == "NHD" else v.transpose(0, 1).contiguous()
+        o, lse = single_decode_with_kv_cache(q, kk, vv, kv_layout=layout, return_lse=True)
+        torch.cuda.synchronize()
+        eo = float(np.abs(o.float().cpu().numpy() - ro[0]).max())
+        el = float(np.abs(lse.cpu().numpy() - rl[0]).max())
+        log(f"single_decode {layout}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+        assert eo <= TOL_O["f16"] and el <= TOL_LSE
+
+
+def test_run_errors():
+    log("case: run-time error paths")
+    w = build(small_spec(p_q=(10,), p_kv=(10,), d_kv=(20,), hqo=8, hkv=2), device="cuda")
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    pod = BatchPOD(ws)
+    with pytest.raises(_lib.PodError):
+        pod.run(w.prefill.q, w.prefill.kv_cache, w.prefill.kv_indices_dev, None, None, None)
+    res, pod = plan_and_run(w, pod=pod)
+    with pytest.raises(_lib.PodError):
+        pod.run(w.prefill.q.half(), w.prefill.kv_cache, w.prefill.kv_indices_dev,
+                w.decode.q, w.decode.kv_cache, w.decode.kv_indices_dev)
+    with pytest.raises(ValueError):
+        pod.run(w.prefill.q, w.prefill.kv_cache, w.prefill.kv_indices_dev,
+                w.decode.q, w.decode.kv_cache, w.decode.kv_indices_dev,
+                sinks=torch.zeros(8, device="cuda"))
+    with pytest.raises(ValueError):
+        pod.run(w.prefill.q[:5], w.prefill.kv_cache, w.prefill.kv_indices_dev,
+                w.decode.q, w.decode.kv_cache, w.decode.kv_indices_dev)
+    # workspace too small for a split plan: one request of 2000 keys in chunks of 64
+    tiny = BatchPOD(torch.empty(4096, dtype=torch.uint8, device="cuda"))
+    with pytest.raises(_lib.PodError):
+        tiny.plan(None, None, None, [0, 1], [0, 125], [16], num_qo_heads=8, num_kv_heads=2,
+                  head_dim=128, page_size=16, decode_chunk=64)
+
+
+# ------------------------------------------------------------ named workloads, full size
+
+
+def sample_rows(qo_len, rng, extra=24):
+    base = {0, 1, 15, 16, 17, 31, 63, 64, 127, 128, qo_len // 2, qo_len - 17, qo_len - 16,
+            qo_len - 2, qo_len - 1}
+    base |= set(rng.integers(0, qo_len, extra).tolist())
+    return np.array(sorted(r for r in base if 0 <= r < qo_len))
+
+
+@pytest.mark.parametrize("name", ["single_decode", "batch_decode", "batch_prefill", "pod"])
+def test_named_workload(name):
+    log(f"case: named workload {name} (full size)")
+    w = build(named_spec(name), device="cuda")
+    res, pod = plan_and_run(w)
+    log(f"plan: {pod.plan_info()}")
+    (op, lp), (od, ld) = res
+    rng = np.random.default_rng(7)
+    if w.prefill is not None:
+        errs = compare_role(w, w.prefill, op, lp,
+                            rows_of=lambda b: sample_rows(int(w.prefill.qo_lens[b]), rng),
+                            tag=name + "/prefill")
+        assert_close(w, errs, name + "/prefill")
+    if w.decode is not None:
+        assert_close(w, compare_role(w, w.decode, od, ld, tag=name + "/decode"), name + "/decode")
+    del w
+    torch.cuda.empty_cache()
+
+
+def test_named_pod_chunked():
+    log("case: named workload pod_chunked (full size, 17.8 GB pool)")
+    w = build(named_spec("pod_chunked"), device="cuda")
+    res, pod = plan_and_run(w)
+    log(f"plan: {pod.plan_info()}")
+    (op, lp), (od, ld) = res
+    rng = np.random.default_rng(5)
+    errs = compare_role(w, w.prefill, op, lp, rows_of=lambda b: sample_rows(4096, rng, 40),
+                        tag="pod_chunked/prefill")
+    assert_close(w, errs, "pod_chunked/prefill")
+    reqs = sorted(set(rng.choice(256, 24, replace=False).tolist()) |
+                  {int(np.argmin(w.decode.kv_lens)), int(np.argmax(w.decode.kv_lens))})
+    errs = compare_role(w, w.decode, od, ld, requests=reqs, tag="pod_chunked/decode")
+    assert_close(w, errs, "pod_chunked/decode")
+    del w
+    torch.cuda.empty_cache()

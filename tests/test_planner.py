@@ -1,0 +1,204 @@
+"""Host planner, driven through pod_plan_compute (no GPU): the work list covers
+every (row, kv head, valid key) exactly once, split groups are consistent,
+items sit on the die their slot maps to, and bad inputs get their error code."""
+import numpy as np
+import pytest
+
+from serving_attention_amd import _lib
+
+from plan_helpers import compute, decode_image, plan_desc
+
+FLAG_ROLE, FLAG_CHUNK = 1, 2
+
+
+def check_coverage(img, roles, hqo, hkv):
+    """roles: list of (qo_lens, kv_lens, causal, window_left) for prefill then decode."""
+    g = hqo // hkv
+    im = decode_image(img)
+    reqs = im["reqs"]
+    items = im["items"]
+    # expected request table
+    exp = []
+    for qo_lens, kv_lens, _, _ in roles:
+        qs = 0
+        for q, k in zip(qo_lens, kv_lens):
+            exp.append((qs, q, k))
+            qs += q
+    assert [tuple(r[:3]) for r in reqs] == exp
+    cover = {}   # (req, kvh) -> count array [qo_len, kv_len]
+    role_of_req = []
+    for r, (qo_lens, kv_lens, causal, w) in enumerate(roles):
+        for q, k in zip(qo_lens, kv_lens):
+            role_of_req.append((r, causal, w))
+    n_real = 0
+    group_members = {}
+    for s, it in enumerate(items):
+        flags = int(it[0])
+        if flags == -1:
+            continue
+        n_real += 1
+        req, kvh, tok0, ntok, kb, ke, grp = [int(x) for x in it[1:]]
+        role, causal, w = role_of_req[req]
+        assert (flags & FLAG_ROLE) == role
+        qo_len, kv_len = int(reqs[req][1]), int(reqs[req][2])
+        c = cover.setdefault((req, kvh), np.zeros((qo_len, kv_len), np.int32))
+        if flags & FLAG_CHUNK:
+            assert tok0 == 0 and ntok == qo_len and qo_len * g <= 32
+            rows = range(qo_len)
+            if grp >= 0:
+                group_members.setdefault(grp, []).append(flags >> 8)
+        else:
+            assert ntok * g <= 128 and grp == -1
+            rows = range(tok0, tok0 + ntok)
+        assert 0 <= kb < ke <= kv_len
+        for i in rows:
+            p = kv_len - qo_len + i
+            lo = max(0, p - w) if w >= 0 else 0
+            hi = p if causal else kv_len - 1
+            # every valid key of the row inside the item's range is counted once
+            c[i, max(kb, lo):min(ke, hi + 1)] += 1
+    assert n_real == im["n_items"]
+    for (req, kvh), c in cover.items():
+        role, causal, w = role_of_req[req]
+        qo_len, kv_len = c.shape
+        for i in range(qo_len):
+            p = kv_len - qo_len + i
+            lo = max(0, p - w) if w >= 0 else 0
+            hi = p if causal else kv_len - 1
+            assert np.all(c[i, lo:hi + 1] == 1), (req, kvh, i)
+    expected_units = sum(hkv for qo_lens, _, _, _ in roles for q in qo_lens if q > 0)
+    assert len(cover) == expected_units
+    # split groups: members 0..n-1, slots disjoint and in range
+    slots = set()
+    for gi, grp in enumerate(im["groups"]):
+        n, first = int(grp[0]), int(grp[1])
+        assert sorted(group_members[gi]) == list(range(n))
+        for s in range(first, first + n):
+            assert s not in slots
+            slots.add(s)
+    assert slots == set(range(im["n_slots"]))
+    assert np.all(im["counters"] == 0)
+    return im
+
+
+@pytest.mark.parametrize("page_size", [1, 16])
+def test_pod_example_coverage(page_size):
+    roles = [([300, 200], [300, 200], True, -1), ([1] * 17, [700] * 17, True, -1)]
+    desc, keep = plan_desc(prefill=dict(qo_lens=roles[0][0], kv_lens=roles[0][1]),
+                           decode=dict(qo_lens=roles[1][0], kv_lens=roles[1][1]),
+                           hqo=32, hkv=4, page_size=page_size)
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    im = check_coverage(img, roles, 32, 4)
+    assert info.n_prefill_items + info.n_decode_items == info.n_items
+    assert info.grid % 8 == 0
+
+
+@pytest.mark.parametrize("w", [-1, 0, 5, 100])
+@pytest.mark.parametrize("chunk", [0, 64, 128, -1])
+def test_window_and_multi_token_decode_coverage(w, chunk):
+    roles = [([64, 1, 0], [500, 77, 20], True, w), ([4, 4, 2, 1], [1053, 90, 4, 33], True, w)]
+    desc, keep = plan_desc(prefill=dict(qo_lens=roles[0][0], kv_lens=roles[0][1], window_left=w),
+                           decode=dict(qo_lens=roles[1][0], kv_lens=roles[1][1], window_left=w),
+                           hqo=16, hkv=2, page_size=16, decode_chunk=chunk)
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    check_coverage(img, roles, 16, 2)
+
+
+def test_non_causal_and_mha_coverage():
+    roles = [([40, 7], [40, 100], False, -1), ([1, 1], [1, 65], False, 3)]
+    desc, keep = plan_desc(prefill=dict(qo_lens=roles[0][0], kv_lens=roles[0][1], causal=False),
+                           decode=dict(qo_lens=roles[1][0], kv_lens=roles[1][1], causal=False, window_left=3),
+                           hqo=4, hkv=4, page_size=3)
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    check_coverage(img, roles, 4, 4)
+
+
+def test_large_group_uses_tiles_for_decode():
+    # group 64: a one-token decode has 64 rows, more than a key chunk holds
+    roles = [([], [], True, -1), ([1, 2], [100, 300], True, -1)]
+    desc, keep = plan_desc(decode=dict(qo_lens=roles[1][0], kv_lens=roles[1][1]), hqo=64, hkv=1)
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    im = check_coverage(img, roles, 64, 1)
+    assert all((int(it[0]) & FLAG_CHUNK) == 0 for it in im["items"] if it[0] != -1)
+
+
+def test_tiles_of_one_kv_unit_share_a_die():
+    desc, keep = plan_desc(prefill=dict(qo_lens=[2048, 2048], kv_lens=[2048, 2048]), hqo=64, hkv=8,
+                           page_size=1)
+    rc, img, info = compute(desc)
+    im = decode_image(img)
+    die = {}
+    for s, it in enumerate(im["items"]):
+        if it[0] == -1:
+            continue
+        key = (int(it[1]), int(it[2]))
+        die.setdefault(key, set()).add(s % 8)
+    assert all(len(v) == 1 for v in die.values())
+
+
+def test_auto_split_gives_enough_items_for_single_decode():
+    desc, keep = plan_desc(decode=dict(qo_lens=[1], kv_lens=[2048], causal=False), hqo=32, hkv=32,
+                           page_size=1)
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    assert info.n_decode_items >= 256 and info.n_groups == 32
+    check_coverage(img, [([], [], True, -1), ([1], [2048], False, -1)], 32, 32)
+
+
+def test_orders_are_permutations_of_the_same_items():
+    base = None
+    for order in (0, 1, 2):
+        desc, keep = plan_desc(prefill=dict(qo_lens=[100, 50], kv_lens=[100, 60]),
+                               decode=dict(qo_lens=[1] * 9, kv_lens=list(range(100, 1000, 100))),
+                               hqo=8, hkv=2, order=order)
+        rc, img, info = compute(desc)
+        im = decode_image(img)
+        items = sorted(tuple(int(x) for x in it[1:7]) for it in im["items"] if it[0] != -1)
+        base = base or items
+        assert items == base
+
+
+def test_workspace_sizes():
+    desc, keep = plan_desc(decode=dict(qo_lens=[1] * 4, kv_lens=[5000] * 4), hqo=8, hkv=1,
+                           decode_chunk=512)
+    rc, img, info = compute(desc)
+    assert info.n_slots == 4 * 10
+    assert info.float_ws_bytes == info.n_slots * (32 * 128 + 32) * 4
+    assert info.int_ws_bytes == info.image_ints * 4
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(hqo=6, hkv=4), _lib.POD_ERR_INVALID),
+    (dict(head_dim=64), _lib.POD_ERR_UNSUPPORTED),
+    (dict(page_size=0), _lib.POD_ERR_INVALID),
+    (dict(dtype=7), _lib.POD_ERR_UNSUPPORTED),
+    (dict(hqo=256, hkv=1), _lib.POD_ERR_UNSUPPORTED),
+    (dict(order=9), _lib.POD_ERR_INVALID),
+])
+def test_invalid_plan_parameters(case, code):
+    args = dict(prefill=dict(qo_lens=[10], kv_lens=[10]), hqo=8, hkv=2)
+    args.update(case)
+    if args.get("page_size", 16) == 0:
+        args["prefill"] = dict(qo_lens=[10], kv_lens=[10], qo_indptr=[0, 10], kv_indptr=[0, 1],
+                               last_page_len=[10])
+    desc, keep = plan_desc(**args)
+    rc, _, _ = compute(desc)
+    assert rc == code
+
+
+@pytest.mark.parametrize("role", [dict(qo_indptr=[1, 10]),
+                                  dict(qo_indptr=[0, 10], kv_indptr=[0, 0]),
+                                  dict(last_page_len=[0]),
+                                  dict(last_page_len=[17]),
+                                  dict(qo_indptr=[0, 40])])
+def test_invalid_page_tables(role):
+    base = dict(qo_lens=[10], kv_lens=[20])
+    base.update(role)
+    desc, keep = plan_desc(prefill=base, hqo=8, hkv=2)
+    rc, _, _ = compute(desc)
+    assert rc == _lib.POD_ERR_INVALID
+    assert _lib.load().pod_last_error()
