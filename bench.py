@@ -1,0 +1,342 @@
+"""POD step benchmark on one MI355X.
+
+A step is one pass of the whole path over one batch: plan() (host work list +
+its upload) followed by one fused run() launch. Inputs are synthetic, seeded
+and resident in HBM before the timed region. Per layer the KV cache and the
+queries differ, as in the per-layer loop of the POD article's examples, so a
+step does not find the previous step's KV in the caches.
+
+Prints one JSON line. `value` is the mean step latency in microseconds.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "POD step latency (µs); prefill TFLOP/s + decode KV HBM GB/s vs roofline"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
+KERNEL_NAME = "pod_grid_kernel"
+
+DESCR = {
+    "single_decode": "single-request decode: q [32,128] fp16, K/V [2048,32,128] fp16, NHD",
+    "batch_decode": "batch paged decode: 7 requests, 64/8 heads, page_size 16, 128 pages, fp16",
+    "batch_prefill": "batch paged causal prefill: 4 requests (1711, 409, 577, 680 tokens), 32/8 heads, "
+                     "page_size 16, shuffled pages, bf16",
+    "pod": "POD fused step: 2 x 2048-token causal prefill + 128 x 1-token decode on 2048 keys, "
+           "64/8 heads, head_dim 128, page_size 1, bf16",
+    "pod_chunked": "chunked-prefill POD: 4096-token chunk on a 16384-token prefix + 256 x 4-token "
+                   "decode (kv 1024..32768), window_left 4096, fp32 sinks, 64/8 heads, page_size 16, bf16",
+}
+
+
+def work_counts(w):
+    """Algorithmic work of one step: FLOPs over valid (row, key) pairs and HBM
+    bytes with every needed K/V row of each kv head counted once."""
+    spec = w.spec
+    D, Hq, Hk = spec.head_dim, spec.num_qo_heads, spec.num_kv_heads
+    eb = 2
+    out = {}
+    for name, r in w.roles():
+        pairs = 0
+        kv_tokens = 0
+        for qo, kv in zip(r.qo_lens, r.kv_lens):
+            if qo == 0:
+                continue
+            lo_first = None
+            for i in range(qo):
+                p = kv - qo + i
+                hi = p if r.causal else kv - 1
+                lo = max(0, p - r.window_left) if r.window_left >= 0 else 0
+                pairs += max(0, hi - lo + 1)
+                lo_first = lo if lo_first is None else min(lo_first, lo)
+            last_hi = kv - 1
+            kv_tokens += last_hi - lo_first + 1
+        rows = sum(r.qo_lens)
+        flops = 4.0 * D * Hq * pairs
+        kv_bytes = float(kv_tokens) * Hk * D * 2 * eb
+        io_bytes = rows * Hq * D * eb * 2 + rows * Hq * 4
+        out[name] = dict(flops=flops, kv_bytes=kv_bytes, io_bytes=io_bytes, rows=rows)
+    return out
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("planner.cpp", "pod_api.cpp", "pod_kernels.hip", "pod_internal.h"):
+        with open(os.path.join(ROOT, "serving_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"pod_grid_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def make_layers(name, n_layers, device):
+    from workloads import build, named_spec
+    layers = []
+    for i in range(n_layers):
+        spec = named_spec(name)
+        spec.value_seed += 7919 * i
+        layers.append(build(spec, device=device))
+    return layers
+
+
+def plan(pod, w, roles, decode_chunk, order):
+    import torch
+    spec = w.spec
+    p = w.prefill if "prefill" in roles else None
+    d = w.decode if "decode" in roles else None
+    pod.plan(p.qo_indptr if p else None, p.kv_indptr if p else None, p.last_page_len if p else None,
+             d.qo_indptr if d else None, d.kv_indptr if d else None, d.last_page_len if d else None,
+             num_qo_heads=spec.num_qo_heads, num_kv_heads=spec.num_kv_heads, head_dim=spec.head_dim,
+             page_size=spec.page_size,
+             dtype={"f16": torch.float16, "bf16": torch.bfloat16}[spec.dtype],
+             causal_p=p.causal if p else True, causal_d=d.causal if d else True,
+             window_left_p=p.window_left if p else -1, window_left_d=d.window_left if d else -1,
+             sm_scale_p=p.sm_scale if p else None, sm_scale_d=d.sm_scale if d else None,
+             sinks=spec.sinks, decode_chunk=decode_chunk, order=order)
+
+
+def run(pod, w, roles, outs):
+    p = w.prefill if "prefill" in roles else None
+    d = w.decode if "decode" in roles else None
+    return pod.run(p.q if p else None, p.kv_cache if p else None, p.kv_indices_dev if p else None,
+                   d.q if d else None, d.kv_cache if d else None, d.kv_indices_dev if d else None,
+                   sinks=w.sinks if w.spec.sinks else None, return_lse=True,
+                   out_p=outs[0][0], lse_p=outs[0][1], out_d=outs[1][0], lse_d=outs[1][1])
+
+
+def alloc_outs(w, roles):
+    import torch
+    res = []
+    for name in ("prefill", "decode"):
+        r = getattr(w, name)
+        if r is None or name not in roles:
+            res.append((None, None))
+        else:
+            res.append((torch.empty_like(r.q),
+                        torch.empty(r.q.shape[:2], dtype=torch.float32, device=r.q.device)))
+    return res
+
+
+def time_kernel(pod, layers, roles, steps, warmup, decode_chunk, order, replan):
+    """Mean launch duration (HIP events on the launch stream) and mean wall step time."""
+    import torch
+    outs = [alloc_outs(w, roles) for w in layers]
+    plan(pod, layers[0], roles, decode_chunk, order)
+    for i in range(warmup):
+        w = layers[i % len(layers)]
+        if replan:
+            plan(pod, w, roles, decode_chunk, order)
+        run(pod, w, roles, outs[i % len(layers)])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    plan_s = 0.0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        w = layers[i % len(layers)]
+        if replan:
+            tp = time.perf_counter()
+            plan(pod, w, roles, decode_chunk, order)
+            plan_s += time.perf_counter() - tp
+        ev[i][0].record(stream)
+        run(pod, w, roles, outs[i % len(layers)])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = [a.elapsed_time(b) * 1e3 for a, b in ev]   # us
+    kern.sort()
+    return dict(step_us=wall / steps * 1e6, kernel_us=sum(kern) / len(kern),
+                kernel_p10_us=kern[len(kern) // 10], kernel_p50_us=kern[len(kern) // 2],
+                kernel_p90_us=kern[min(len(kern) - 1, (9 * len(kern)) // 10)],
+                plan_us=plan_s / steps * 1e6 if replan else None)
+
+
+def cpu_baseline(w, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same step,
+    scaled to a whole step. Returns the dict of the cpu_baseline field."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+    except Exception:
+        pass
+    spec = w.spec
+    sinks = w.sinks.cpu().numpy() if spec.sinks else None
+    est = 0.0
+    parts = []
+    for name, r in w.roles():
+        # host copies of a few requests' pages, made before the clock starts
+        rng = np.random.default_rng(0)
+        order = rng.permutation(r.batch)
+        t_role, rows_done, rows_total = 0.0, 0, sum(r.qo_lens)
+        for b in order:
+            if t_role > budget_s / 2 and rows_done > 0:
+                break
+            p0, p1 = int(r.kv_indptr[b]), int(r.kv_indptr[b + 1])
+            idx = torch.from_numpy(r.kv_indices[p0:p1].astype(np.int64)).to(r.k_pool.device)
+            kp = r.k_pool.index_select(0, idx).float().cpu().numpy()
+            vp = r.v_pool.index_select(0, idx).float().cpu().numpy()
+            q0, q1 = int(r.qo_indptr[b]), int(r.qo_indptr[b + 1])
+            q = r.q[q0:q1].float().cpu().numpy()
+            qo = q1 - q0
+            # long requests: a block of consecutive rows (every row costs the same in the oracle)
+            nrows = qo if qo <= 64 else 64
+            t = time.perf_counter()
+            oracle.attend_role(q, kp, vp, np.array([0, qo]), np.array([0, p1 - p0]), None,
+                               r.last_page_len[b:b + 1], spec.page_size, spec.num_qo_heads,
+                               spec.num_kv_heads, r.causal, r.window_left, r.sm_scale, sinks,
+                               rows_of=lambda _: np.arange(qo - nrows, qo))
+            t_role += time.perf_counter() - t
+            rows_done += nrows
+        est += t_role * rows_total / rows_done
+        parts.append(f"{name}: {rows_done} of {rows_total} rows")
+    return {"value": est * 1e6, "unit": "us", "cores": threads or os.cpu_count(),
+            "kind": "oracle",
+            "sample": "fp64 numpy oracle timed on " + "; ".join(parts) +
+                      " (last rows of randomly chosen requests), scaled by rows to one step",
+            "host_cpus": os.cpu_count(), "host": platform.processor() or platform.machine()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="pod", choices=sorted(DESCR))
+    ap.add_argument("--layers", type=int, default=None,
+                    help="distinct KV caches / queries cycled per step (default: 4, 1 for pod_chunked)")
+    ap.add_argument("--decode-chunk", type=int, default=0)
+    ap.add_argument("--order", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-roles", action="store_true", help="skip the role-isolated launches")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 1 GiB device copies (for scaling rocprofv3 byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the path has no multi-GPU component; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from serving_attention_amd import BatchPOD
+
+    if args.copy_calibration:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": a.numel() * 4, "copies": 3}))
+        return
+
+    n_layers = args.layers or (1 if args.workload == "pod_chunked" else 4)
+    layers = make_layers(args.workload, n_layers, "cuda")
+    w0 = layers[0]
+    ws = torch.empty(128 << 20, dtype=torch.uint8, device="cuda")
+    pod = BatchPOD(ws, w0.spec.kv_layout, int_workspace_bytes=8 << 20)
+    all_roles = tuple(n for n, _ in w0.roles())
+
+    main_t = time_kernel(pod, layers, all_roles, args.steps, args.warmup, args.decode_chunk,
+                         args.order, replan=True)
+    info = pod.plan_info()
+    work = work_counts(w0)
+    flops_p = work.get("prefill", {}).get("flops", 0.0)
+    kv_all = sum(v["kv_bytes"] for v in work.values())
+    io_all = sum(v["io_bytes"] for v in work.values())
+    k_us = main_t["kernel_us"]
+    t_star = max(flops_p / (PEAK_BF16_TFLOPS * 1e12), (kv_all + io_all) / (PEAK_HBM_GBS * 1e9)) * 1e6
+
+    roles_out = {}
+    if not args.no_roles and len(all_roles) == 2:
+        for name in all_roles:
+            t = time_kernel(pod, layers, (name,), max(5, args.steps // 2), 2, args.decode_chunk,
+                            args.order, replan=False)
+            wk = work[name]
+            roles_out[name] = dict(
+                kernel_us=t["kernel_us"],
+                tflops=wk["flops"] / (t["kernel_us"] * 1e-6) / 1e12,
+                kv_gbs=wk["kv_bytes"] / (t["kernel_us"] * 1e-6) / 1e9,
+                hbm_gbs=(wk["kv_bytes"] + wk["io_bytes"]) / (t["kernel_us"] * 1e-6) / 1e9)
+        plan(pod, w0, all_roles, args.decode_chunk, args.order)
+
+    algo_bytes = kv_all + io_all
+    bound = "hbm" if (kv_all + io_all) / (PEAK_HBM_GBS * 1e9) >= flops_p / (PEAK_BF16_TFLOPS * 1e12) else "mfma"
+    if bound == "hbm":
+        achieved = algo_bytes / (k_us * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = flops_p / (k_us * 1e-6) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    roof["traffic"] = committed_traffic(args.workload)
+    roof["algorithmic_bytes_per_launch"] = algo_bytes
+    roof["kernel"] = KERNEL_NAME
+    roof["kernel_us"] = k_us
+
+    result = {
+        "metric": METRIC,
+        "value": main_t["step_us"],
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_t["step_us"] / 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w0.spec.dtype,
+        "data": "synthetic (seeded N(0,1) values, lengths and page tables of the named workload)",
+        "config": {"workload": args.workload, "description": DESCR[args.workload],
+                   "layers_cycled": n_layers, "decode_chunk": info["decode_chunk"],
+                   "order": args.order, "items": info["n_items"], "grid": info["grid"]},
+        "kernel_us": k_us,
+        "kernel_p10_us": main_t["kernel_p10_us"],
+        "kernel_p90_us": main_t["kernel_p90_us"],
+        "plan_us": main_t["plan_us"],
+        "prefill_tflops": flops_p / (k_us * 1e-6) / 1e12 if flops_p else None,
+        "decode_kv_gbs": work["decode"]["kv_bytes"] / (k_us * 1e-6) / 1e9 if "decode" in work else None,
+        "t_star_us": t_star,
+        "t_star_frac": t_star / k_us,
+        "roles_isolated": roles_out or None,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w0, args.cpu_budget)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
