@@ -289,6 +289,9 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
   p.num_kv_heads = ctx->num_kv_heads;
   p.group_size = ctx->num_qo_heads / ctx->num_kv_heads;
   p.page_size = ctx->page_size;
+  p.page_shift = -1;
+  for (int sh = 0; sh < 31; ++sh)
+    if ((1 << sh) == ctx->page_size) p.page_shift = sh;
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
   int e = pod::launch_pod_grid(p, ctx->dtype, ctx->info.grid, stream);

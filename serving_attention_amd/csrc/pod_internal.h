@@ -51,6 +51,7 @@ struct Params {
   int32_t num_kv_heads;
   int32_t group_size;
   int32_t page_size;
+  int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
 };
 
 // Launch the fused grid on `stream` (a hipStream_t). Returns a hipError_t value.

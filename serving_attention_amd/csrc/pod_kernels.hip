@@ -1,28 +1,35 @@
 // Fused Prefill-On-Decode paged attention for gfx950 (MI355X, CDNA4).
 //
 // One launch runs every item of the planner's work list: query tiles (prefill
-// style: up to 128 rows share each staged K/V block) and key chunks (decode
-// style: the q_len x group rows of one request and kv head share every K/V row
-// read from HBM, the keys are split over the 4 waves and over workgroups).
+// style: up to 128 rows share each K/V block staged in LDS) and key chunks
+// (decode style: the q_len x group rows of one request and kv head share every
+// K/V row read from HBM; keys are split over the 4 waves and over workgroups).
 // This is the "prefill and decode in one launch" idea of the POD article
 // (www.dpshk.com/news/5405057, "POD 是什么"), built for wave64 and MFMA.
 //
 // Math per row (cuDNN backend article www.gsyq.cn/news/452757, "LSE 契约" and
 // "Decode 能力矩阵与参数"): scores s_j = sm_scale * q.k_j over the row's valid
 // keys, O = sum_j softmax_j v_j with an optional sink logit in the
-// denominator, lse = log2 sum_j exp(s_j). Work is done in the base-2 domain:
-// t_j = s_j * log2(e), online max / sum with exp2, and partial states over
-// disjoint key ranges merge as L = log2 sum 2^lse_k, O = sum 2^(lse_k - L) O_k.
+// denominator, lse = log2 sum_j exp(s_j). The online softmax keeps the running
+// max in raw score units and evaluates exp2(s * sm_scale * log2(e) - m'); partial
+// states over disjoint key ranges merge as L = log2 sum 2^lse_k,
+// O = sum 2^(lse_k - L) O_k.
 //
 // MFMA formulation (v_mfma_f32_32x32x16_{bf16,f16}):
-//   S^T[key][row] = K[key][:] . Q[row][:]   A = K rows, B = Q^T (in registers)
-//   O^T[d][row]  += V^T[d][key] . P^T[key][row]   A = V^T (LDS), B = P^T (registers)
-// The accumulator keeps one query row per lane column, so the softmax row
-// statistics are per-lane scalars plus one exchange between the two lane
-// halves. K rows are assigned to MFMA rows with bits 2 and 3 of the row index
-// swapped, which makes the score accumulator registers of each lane half hold
-// 8 consecutive keys: the P^T operand then comes straight from the
-// accumulators, and V^T is read as 16 contiguous bytes per lane.
+//   S^T[key][row] = K[key][:] . Q[row][:]          A = K rows, B = Q^T (registers)
+//   O^T[d][row]  += V^T[d][key] . P^T[key][row]    A = V^T, B = P^T (registers)
+// The accumulators hold one query row per lane column, so the softmax row
+// statistics are per-lane scalars plus one exchange between the lane halves
+// (v_permlane32_swap). K rows are assigned to MFMA rows with bits 2 and 3 of
+// the row index swapped, so each lane half's score accumulators cover 8
+// consecutive keys and the P^T operand comes straight from them.
+//
+// LDS layout: K and V blocks are row-major, one 256-byte row per key (one kv
+// head's 128 dims), with the 16-byte chunks of row `key` permuted by
+// XOR with swz(key). Sixteen consecutive keys then put any fixed chunk in 16
+// distinct bank groups (conflict-free row writes and K operand reads), and the
+// 4-key x 16-dim blocks read by ds_read_b64_tr_b16 for the V^T operand fall in
+// disjoint banks for the two 16-lane groups of each half wave.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -34,11 +41,13 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_inff();
@@ -62,14 +71,11 @@ struct Dt<_Float16> {
   }
 };
 
-// LDS geometry (element counts; rows padded by 8 elements = 16 bytes)
-constexpr int kTileKeys = 64;                 // keys per staged block of a query tile
-constexpr int kKsStride = kHeadDim + 8;       // K block [64 keys][136]
-constexpr int kVtStride = kTileKeys + 8;      // V^T block [128 d][72]
-constexpr int kChunkKeys = 32;                // keys per wave step of a key chunk
-constexpr int kCvStride = kChunkKeys + 8;     // per-wave V^T block [128 d][40]
-constexpr int kTileLds = (kTileKeys * kKsStride + kHeadDim * kVtStride) * 2;
-constexpr int kChunkLds = 4 * kHeadDim * kCvStride * 2;
+constexpr int kRowBytes = kHeadDim * 2;       // one kv head's K or V row (16-bit types)
+constexpr int kTileKeys = 64;                 // keys per LDS block of a query tile
+constexpr int kStepKeys = 32;                 // keys per wave step of a key chunk
+constexpr int kTileLds = 2 * kTileKeys * kRowBytes;          // K + V block: 32 KB
+constexpr int kChunkLds = 4 * kStepKeys * kRowBytes;         // 4 per-wave V blocks: 32 KB
 constexpr int kMergeLds = (4 * 32 * 2 + 2 * kHeadDim * 32) * 4 + 16;
 constexpr int kLdsBytes = kTileLds > kChunkLds ? (kTileLds > kMergeLds ? kTileLds : kMergeLds)
                                                : (kChunkLds > kMergeLds ? kChunkLds : kMergeLds);
@@ -77,18 +83,61 @@ constexpr int kLdsBytes = kTileLds > kChunkLds ? (kTileLds > kMergeLds ? kTileLd
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// MFMA row m of the score block holds key swap_bits23(m) of the 32-key group.
+// Value from the other lane half (lane ^ 32) combined with the own value.
+__device__ __forceinline__ float xhalf_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// MFMA row m of a 32-key score block holds key key_row(m) of that block.
 __device__ __forceinline__ int key_row(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
-// key (within a 32-key group) held by score accumulator j of lane half hi
+// key (within a 32-key block) held by score accumulator j of lane half hi
 __device__ __forceinline__ int acc_key(int j, int hi) { return 16 * (j >> 3) + 8 * hi + (j & 7); }
-// head-dim index held by output accumulator j (of a 32-wide d block) of lane half hi
+// head-dim index (within a 32-wide block) held by output accumulator j of lane half hi
 __device__ __forceinline__ int acc_d(int j, int hi) { return 8 * (j >> 2) + 4 * hi + (j & 3); }
+
+// chunk permutation of LDS row `key` (depends on key % 16 only)
+__device__ __forceinline__ int swz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
+// byte offset of 16-byte chunk `chunk` of row `key` in a swizzled block
+__device__ __forceinline__ int row_chunk(int key, int chunk) {
+  return key * kRowBytes + ((chunk ^ swz(key)) << 4);
+}
 
 template <typename T>
 __device__ __forceinline__ u32x4 ld16(const T* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x4 lds_ld16(const char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+__device__ __forceinline__ void lds_st16(char* base, int off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(base + off) = v;
+}
+
+// V^T operand of one 32x32x16 MFMA: lane (d = l % 32, half hi = l / 32) gets
+// V[key0 + 8*hi + e][d0 + l % 32], e = 0..7, from a swizzled row-major block.
+// Two transpose reads, each serving 4 keys x 16 dims per 16-lane group.
+template <typename V8>
+__device__ __forceinline__ V8 vt_operand(const char* blk, int key0, int d0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int dchunk = (d0 >> 3) + 2 * (g & 1) + ((i & 3) >> 1);
+  const int half = 8 * (i & 1);
+  u32x2 part[2];
+#pragma unroll
+  for (int ld = 0; ld < 2; ++ld) {
+    const int key = key0 + 8 * (g >> 1) + 4 * ld + (i >> 2);
+    const LDS_AS char* p = (const LDS_AS char*)blk + row_chunk(key, dchunk) + half;
+    i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p);
+    part[ld] = __builtin_bit_cast(u32x2, v);
+  }
+  u32x4 w = {part[0][0], part[0][1], part[1][0], part[1][1]};
+  return __builtin_bit_cast(V8, w);
 }
 
 struct RowGeom {
@@ -133,15 +182,21 @@ __device__ __forceinline__ RoleView pick_role(const Params& p, int role) {
 }
 
 // Element offset of (logical key, kv head) in a role's pool.
-__device__ __forceinline__ int64_t kv_offset(const RoleView& r, int page_size, int page_start,
+__device__ __forceinline__ int64_t kv_offset(const RoleView& r, const Params& p, int page_start,
                                              int key, int kvh) {
-  int pg = key / page_size;
-  int slot = key - pg * page_size;
-  int64_t page = r.indices ? (int64_t)r.indices[page_start + pg] : (int64_t)(page_start + pg);
+  int pg, slot;
+  if (p.page_shift >= 0) {
+    pg = key >> p.page_shift;
+    slot = key & (p.page_size - 1);
+  } else {
+    pg = key / p.page_size;
+    slot = key - pg * p.page_size;
+  }
+  const int64_t page = r.indices ? (int64_t)r.indices[page_start + pg] : (int64_t)(page_start + pg);
   return page * r.kv_sp + (int64_t)slot * r.kv_st + (int64_t)kvh * r.kv_sh;
 }
 
-// Load the Q^T operand of one row: lane half hi holds d = hi*64 + c*8 + [0,8) for MFMA c.
+// Q^T operand of one row: lane half hi holds d = hi*64 + c*8 + [0,8) for MFMA c.
 template <typename T>
 __device__ __forceinline__ void load_q(typename Dt<T>::v8 (&qreg)[8], const RoleView& r,
                                        bool ok, int tok_global, int head, int hi) {
@@ -154,25 +209,27 @@ __device__ __forceinline__ void load_q(typename Dt<T>::v8 (&qreg)[8], const Role
   }
 }
 
-// Online-softmax update for one block of score accumulators (base-2 domain).
-// s: raw scores (already masked to -inf); returns P as operand vectors.
+// Online-softmax update for NB score blocks of one lane (raw scores, masked
+// entries already -inf). m is kept in raw units; returns P as MFMA operands.
 template <typename T, int NB>
-__device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float& m, float& l,
+__device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float sl2, float& m, float& l,
                                              f32x16 (&o)[4], typename Dt<T>::v8 (&pb)[NB][2]) {
   float mx = kNegInf;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[b][j]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = xhalf_max(mx);
   const float mn = fmaxf(m, mx);
-  const float mu = (mn == kNegInf) ? 0.f : mn;
-  const float alpha = fast_exp2(m - mu);
-  l *= alpha;
+  const float mu2 = (mn == kNegInf) ? 0.f : mn * sl2;
+  const float alpha = fast_exp2(m * sl2 - mu2);
+  if (__any(alpha != 1.f)) {
+    l *= alpha;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
+      for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
+  }
   m = mn;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -180,7 +237,7 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float& m, float& l
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float e = fast_exp2(s[b][8 * h + i] - mu);
+        const float e = fast_exp2(fmaf(s[b][8 * h + i], sl2, -mu2));
         l += e;
         pb[b][h][i] = (T)e;
       }
@@ -188,7 +245,8 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float& m, float& l
 
 // ----------------------------------------------------------------------------
 // Query tile: up to 128 rows (tokens x group heads) of one request and kv head,
-// keys [kv_begin, kv_end) in blocks of 64 staged in LDS by all 4 waves.
+// keys [kv_begin, kv_end) in 64-key blocks staged in LDS. The next block's
+// global loads are issued before the current block's MFMA work.
 template <typename T>
 __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg, int kvh, int tok0,
                           int ntok, int kv_begin, int kv_end, char* smem) {
@@ -209,72 +267,102 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   const int key_hi = r.causal ? pdiag : rg.kv_len - 1;
   const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
 
-  T* Ks = reinterpret_cast<T*>(smem);
-  T* Vt = Ks + kTileKeys * kKsStride;
+  char* Ks = smem;
+  char* Vs = smem + kTileKeys * kRowBytes;
+  const T* kbase = reinterpret_cast<const T*>(r.k);
+  const T* vbase = reinterpret_cast<const T*>(r.v);
+
+  // staging: thread t moves rows (t >> 4) + 16 i, chunk slot t & 15
+  const int st_key = threadIdx.x >> 4, st_slot = threadIdx.x & 15;
+  u32x4 kst[4], vst[4];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = st_key + 16 * i;
+      const int kidx = kb + key;
+      if (kidx < kv_end) {
+        const int64_t off = kv_offset(r, p, rg.page_start, kidx, kvh) + ((st_slot ^ swz(key)) << 3);
+        kst[i] = ld16(kbase + off);
+        vst[i] = ld16(vbase + off);
+      } else {
+        kst[i] = u32x4{0, 0, 0, 0};
+        vst[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int off = (st_key + 16 * i) * kRowBytes + (st_slot << 4);
+      lds_st16(Ks, off, kst[i]);
+      lds_st16(Vs, off, vst[i]);
+    }
+  };
+
+  // K operand offsets: lane reads row key_row(r32) (+32 h), chunk hi*8 + c
+  const int krow = key_row(r32);
+  int koff[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) koff[c] = row_chunk(krow, hi * 8 + c);
+
   f32x16 o[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) o[b] = f32x16{};
   float m = kNegInf, l = 0.f;
   const float sl2 = r.scale_log2;
-  const int krow = key_row(r32);
-  const T* kbase = reinterpret_cast<const T*>(r.k);
-  const T* vbase = reinterpret_cast<const T*>(r.v);
 
+  if (kv_begin < kv_end) {
+    load_block(kv_begin);
+    store_block();
+  }
+  __syncthreads();
   for (int kb = kv_begin; kb < kv_end; kb += kTileKeys) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = threadIdx.x + kThreads * i;
-      const int key = idx >> 4, ch = idx & 15;
-      const int kidx = kb + key;
-      u32x4 kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-      if (kidx < kv_end) {
-        const int64_t off = kv_offset(r, p.page_size, rg.page_start, kidx, kvh) + ch * 8;
-        kx = ld16(kbase + off);
-        vx = ld16(vbase + off);
-      }
-      *reinterpret_cast<u32x4*>(Ks + key * kKsStride + ch * 8) = kx;
-      V8 ve = __builtin_bit_cast(V8, vx);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[(ch * 8 + j) * kVtStride + key] = ve[j];
-    }
-    __syncthreads();
+    const bool has_next = kb + kTileKeys < kv_end;
+    if (has_next) load_block(kb + kTileKeys);
 
     f32x16 s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       s[h] = f32x16{};
-      const T* kr = Ks + (h * 32 + krow) * kKsStride + hi * 64;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        s[h] = Dt<T>::mfma(__builtin_bit_cast(V8, ld16(kr + c * 8)), qreg[c], s[h]);
+        s[h] = Dt<T>::mfma(__builtin_bit_cast(V8, lds_ld16(Ks, h * 32 * kRowBytes + koff[c])),
+                           qreg[c], s[h]);
     }
+    const bool need_mask =
+        __any(kb < key_lo || kb + kTileKeys - 1 > key_hi || kb + kTileKeys > kv_end);
+    if (need_mask) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int kidx = kb + h * 32 + acc_key(j, hi);
-        const bool ok = kidx >= key_lo && kidx <= key_hi && kidx < kv_end;
-        s[h][j] = ok ? s[h][j] * sl2 : kNegInf;
-      }
+        for (int j = 0; j < 16; ++j) {
+          const int kidx = kb + h * 32 + acc_key(j, hi);
+          const bool ok = kidx >= key_lo && kidx <= key_hi && kidx < kv_end;
+          s[h][j] = ok ? s[h][j] : kNegInf;
+        }
+    }
     V8 pb[2][2];
-    softmax_step<T, 2>(s, m, l, o, pb);
+    softmax_step<T, 2>(s, sl2, m, l, o, pb);
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const T* vp = Vt + (db * 32 + r32) * kVtStride + h * 32 + 16 * mp + 8 * hi;
-          o[db] = Dt<T>::mfma(__builtin_bit_cast(V8, ld16(vp)), pb[h][mp], o[db]);
-        }
+        for (int db = 0; db < 4; ++db)
+          o[db] = Dt<T>::mfma(vt_operand<V8>(Vs, h * 32 + 16 * mp, db * 32, lane), pb[h][mp], o[db]);
+
+    if (has_next) {
+      __syncthreads();
+      store_block();
+      __syncthreads();
+    }
   }
-  l += __shfl_xor(l, 32);
+  l = xhalf_sum(l);
 
   if (row_ok) {
-    const float mu = (m == kNegInf) ? 0.f : m;
+    const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
     float den = l;
-    if (p.sinks) den += fast_exp2(p.sinks[head] * kLog2e - mu);
+    if (p.sinks) den += fast_exp2(p.sinks[head] * kLog2e - mu2);
     const float inv = den > 0.f ? 1.f / den : 0.f;
     T* op = reinterpret_cast<T*>(r.out) + (int64_t)(rg.qo_start + tok) * r.o_st +
             (int64_t)head * r.o_sh;
@@ -289,15 +377,18 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
       }
     if (r.lse && hi == 0)
       r.lse[(int64_t)(rg.qo_start + tok) * p.num_qo_heads + head] =
-          l > 0.f ? m + fast_log2(l) : kNegInf;
+          l > 0.f ? mu2 + fast_log2(l) : kNegInf;
   }
 }
 
 // ----------------------------------------------------------------------------
 // Key chunk: all q_len x group rows (<= 32) of one request and kv head over keys
-// [kv_begin, kv_end). Wave w takes 32-key steps w, w+4, ...; K goes straight
-// from HBM into MFMA operand registers, V through a per-wave transposed LDS
-// block. Wave states merge in LDS; split chunks merge through the workspace.
+// [kv_begin, kv_end). Wave w takes 32-key steps w, w+4, ... Lane (r, hi) loads
+// K and V of key key_row(r) of the step (its own 128 contiguous bytes of each):
+// K stays in registers as the MFMA A operand, V goes to the wave's LDS block
+// for the transpose reads. The next step's K/V loads are in flight while the
+// current step computes, and the page index is fetched one step further ahead.
+// Wave states merge in LDS; split chunks merge through the float workspace.
 template <typename T>
 __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg, int kvh,
                            int kv_begin, int kv_end, int split, int grp, char* smem) {
@@ -317,7 +408,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   const int key_hi = r.causal ? pdiag : rg.kv_len - 1;
   const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
 
-  T* Vt = reinterpret_cast<T*>(smem) + wave * (kHeadDim * kCvStride);
+  char* vblk = smem + wave * (kStepKeys * kRowBytes);
   f32x16 o[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) o[b] = f32x16{};
@@ -326,68 +417,75 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   const int krow = key_row(r32);
   const T* kbase = reinterpret_cast<const T*>(r.k);
   const T* vbase = reinterpret_cast<const T*>(r.v);
+  int voff[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) voff[c] = row_chunk(krow, hi * 8 + c);
 
-  for (int kb = kv_begin + kChunkKeys * wave; kb < kv_end; kb += 4 * kChunkKeys) {
-    V8 ak[8];
-    {
-      const int key = kb + krow;
-      if (key < kv_end) {
-        const T* kp = kbase + kv_offset(r, p.page_size, rg.page_start, key, kvh) + hi * 64;
+  const int first = kv_begin + kStepKeys * wave;
+  const int n_steps = first < kv_end ? (kv_end - first + 4 * kStepKeys - 1) / (4 * kStepKeys) : 0;
+  // element offset of this lane's key for step i, or -1 past the chunk
+  auto lane_off = [&](int i) -> int64_t {
+    const int key = first + 4 * kStepKeys * i + krow;
+    return key < kv_end ? kv_offset(r, p, rg.page_start, key, kvh) + hi * 64 : (int64_t)-1;
+  };
+  auto load_k = [&](u32x4 (&kx)[8], int64_t off) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) ak[c] = __builtin_bit_cast(V8, ld16(kp + c * 8));
-      } else {
+    for (int c = 0; c < 8; ++c) kx[c] = off >= 0 ? ld16(kbase + off + c * 8) : u32x4{0, 0, 0, 0};
+  };
+  auto load_v = [&](u32x4 (&vx)[8], int64_t off) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) ak[c] = __builtin_bit_cast(V8, u32x4{0, 0, 0, 0});
-      }
-    }
-    u32x4 vx[8];
+    for (int c = 0; c < 8; ++c) vx[c] = off >= 0 ? ld16(vbase + off + c * 8) : u32x4{0, 0, 0, 0};
+  };
+
+  // K double-buffered in registers; V single-buffered (its registers are free
+  // again once the step's V is in LDS, before the next step's V is loaded)
+  u32x4 ka[8], kb_[8], vr[8];
+  int64_t off_next = -1;
+  if (n_steps > 0) {
+    const int64_t off0 = lane_off(0);
+    load_k(ka, off0);
+    load_v(vr, off0);
+    if (n_steps > 1) off_next = lane_off(1);
+  }
+
+  auto step = [&](int i, u32x4 (&kc)[8], u32x4 (&kn)[8]) {
+    const int kb = first + 4 * kStepKeys * i;
+    // V of this step to the wave's block; the previous step's reads of it are
+    // ordered before these writes (LDS executes a wave's requests in order)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = lane + 64 * i;
-      const int kidx = kb + (idx >> 4);
-      vx[i] = kidx < kv_end
-                  ? ld16(vbase + kv_offset(r, p.page_size, rg.page_start, kidx, kvh) + (idx & 15) * 8)
-                  : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < 8; ++c) lds_st16(vblk, voff[c], vr[c]);
+    if (i + 1 < n_steps) {
+      load_k(kn, off_next);
+      load_v(vr, off_next);
+      off_next = (i + 2 < n_steps) ? lane_off(i + 2) : (int64_t)-1;
     }
     f32x16 s[1];
     s[0] = f32x16{};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s[0] = Dt<T>::mfma(ak[c], qreg[c], s[0]);
-
-    // this wave's previous V^T reads are done before it is overwritten
-    __builtin_amdgcn_wave_barrier();
+    for (int c = 0; c < 8; ++c) s[0] = Dt<T>::mfma(__builtin_bit_cast(V8, kc[c]), qreg[c], s[0]);
+    const bool need_mask =
+        __any(kb < key_lo || kb + kStepKeys - 1 > key_hi || kb + kStepKeys > kv_end);
+    if (need_mask) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = lane + 64 * i;
-      const int key = idx >> 4, ch = idx & 15;
-      V8 ve = __builtin_bit_cast(V8, vx[i]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Vt[(ch * 8 + j) * kCvStride + key] = ve[j];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int kidx = kb + acc_key(j, hi);
-      const bool ok = kidx >= key_lo && kidx <= key_hi && kidx < kv_end;
-      s[0][j] = ok ? s[0][j] * sl2 : kNegInf;
+      for (int j = 0; j < 16; ++j) {
+        const int kidx = kb + acc_key(j, hi);
+        const bool ok = kidx >= key_lo && kidx <= key_hi && kidx < kv_end;
+        s[0][j] = ok ? s[0][j] : kNegInf;
+      }
     }
     V8 pb[1][2];
-    softmax_step<T, 1>(s, m, l, o, pb);
+    softmax_step<T, 1>(s, sl2, m, l, o, pb);
 #pragma unroll
     for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const T* vp = Vt + (db * 32 + r32) * kCvStride + 16 * mp + 8 * hi;
-        o[db] = Dt<T>::mfma(__builtin_bit_cast(V8, ld16(vp)), pb[0][mp], o[db]);
-      }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int db = 0; db < 4; ++db)
+        o[db] = Dt<T>::mfma(vt_operand<V8>(vblk, 16 * mp, db * 32, lane), pb[0][mp], o[db]);
+  };
+  for (int i = 0; i < n_steps; i += 2) {
+    step(i, ka, kb_);
+    if (i + 1 < n_steps) step(i + 1, kb_, ka);
   }
-  l += __shfl_xor(l, 32);
+  l = xhalf_sum(l);
 
   // ---- merge the 4 wave states in LDS
   __syncthreads();
@@ -396,10 +494,12 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   float* accA = sm_l + 128;                       // [128 d][32 rows]
   float* accB = accA + kHeadDim * 32;
   int* sm_flag = reinterpret_cast<int*>(accB + kHeadDim * 32);
-  if (hi == 0) sm_m[wave * 32 + r32] = m;
+  // wave maxima in scaled (base-2) units
+  const float m2 = (m == kNegInf) ? kNegInf : m * sl2;
+  if (hi == 0) sm_m[wave * 32 + r32] = m2;
   __syncthreads();
-  float M = fmaxf(fmaxf(sm_m[r32], sm_m[32 + r32]), fmaxf(sm_m[64 + r32], sm_m[96 + r32]));
-  const float sc = (M == kNegInf) ? 0.f : fast_exp2(m - M);
+  const float M = fmaxf(fmaxf(sm_m[r32], sm_m[32 + r32]), fmaxf(sm_m[64 + r32], sm_m[96 + r32]));
+  const float sc = (M == kNegInf) ? 0.f : fast_exp2(m2 - M);
   if (hi == 0) sm_l[wave * 32 + r32] = l * sc;
   float* acc = (wave & 1) ? accB : accA;
   if (wave < 2) {
@@ -485,8 +585,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
     if (Mx != kNegInf) {
       for (int s = 0; s < n_splits; ++s) {
         const float* sl = base + (int64_t)s * kSlotFloats;
-        const float ls = sl[kChunkRows * kHeadDim + frow];
-        const float w = fast_exp2(ls - Mx);
+        const float w = fast_exp2(sl[kChunkRows * kHeadDim + frow] - Mx);
         tot += w;
         const float4* src = reinterpret_cast<const float4*>(sl + frow * kHeadDim + d0);
 #pragma unroll
