@@ -239,6 +239,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-roles", action="store_true", help="skip the role-isolated launches")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--only", choices=("prefill", "decode"), default=None,
+                    help="time launches that carry one role only (for per-role profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device copies (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -266,11 +268,13 @@ def main():
     ws = torch.empty(128 << 20, dtype=torch.uint8, device="cuda")
     pod = BatchPOD(ws, w0.spec.kv_layout, int_workspace_bytes=8 << 20)
     all_roles = tuple(n for n, _ in w0.roles())
+    if args.only:
+        all_roles = (args.only,)
 
     main_t = time_kernel(pod, layers, all_roles, args.steps, args.warmup, args.decode_chunk,
                          args.order, replan=True)
     info = pod.plan_info()
-    work = work_counts(w0)
+    work = {k: v for k, v in work_counts(w0).items() if k in all_roles}
     flops_p = work.get("prefill", {}).get("flops", 0.0)
     kv_all = sum(v["kv_bytes"] for v in work.values())
     io_all = sum(v["io_bytes"] for v in work.values())

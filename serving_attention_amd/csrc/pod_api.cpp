@@ -258,6 +258,10 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
       if ((mis & 15) || (smis & 7))
         return set_err(POD_ERR_INVALID, std::string(names[r]) +
                                              ": buffers must be 16-byte aligned and strides multiples of 8 elements");
+      const int64_t lim = (int64_t)1 << 30;   // bytes = 2 * elements must stay below 2^31
+      if (a.kv_stride_page >= lim || a.kv_stride_tok >= lim || a.kv_stride_head >= lim)
+        return set_err(POD_ERR_UNSUPPORTED, std::string(names[r]) +
+                                                ": KV pool strides must be below 2^30 elements");
       if (a.lse && (reinterpret_cast<uintptr_t>(a.lse) & 3))
         return set_err(POD_ERR_INVALID, std::string(names[r]) + ": lse must be 4-byte aligned");
     }
@@ -266,9 +270,9 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     o.q_sh = a.q_stride_head;
     o.k = a.k_cache;
     o.v = a.v_cache;
-    o.kv_sp = a.kv_stride_page;
-    o.kv_st = a.kv_stride_tok;
-    o.kv_sh = a.kv_stride_head;
+    o.kv_sp_b = (uint32_t)(a.kv_stride_page * 2);
+    o.kv_st_b = (uint32_t)(a.kv_stride_tok * 2);
+    o.kv_sh_b = (uint32_t)(a.kv_stride_head * 2);
     o.indices = a.kv_indices;
     o.out = a.out;
     o.o_st = a.out_stride_tok;

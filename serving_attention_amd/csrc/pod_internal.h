@@ -29,7 +29,7 @@ struct RoleParams {
   int64_t q_st, q_sh;
   const void* k;
   const void* v;
-  int64_t kv_sp, kv_st, kv_sh;
+  uint32_t kv_sp_b, kv_st_b, kv_sh_b;   // pool strides in bytes (< 2^31)
   const int32_t* indices;   // nullptr = identity page table
   void* out;
   int64_t o_st, o_sh;

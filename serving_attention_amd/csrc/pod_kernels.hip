@@ -71,14 +71,20 @@ struct Dt<_Float16> {
   }
 };
 
-constexpr int kRowBytes = kHeadDim * 2;       // one kv head's K or V row (16-bit types)
+constexpr int kRowBytes = kHeadDim * 2;       // one kv head's K row (16-bit types)
+constexpr int kVRowBytes = kRowBytes + 64;    // V rows are padded by 64 bytes
 constexpr int kTileKeys = 64;                 // keys per LDS block of a query tile
 constexpr int kStepKeys = 32;                 // keys per wave step of a key chunk
-constexpr int kTileLds = 2 * kTileKeys * kRowBytes;          // K + V block: 32 KB
-constexpr int kChunkLds = 4 * kStepKeys * kRowBytes;         // 4 per-wave V blocks: 32 KB
+constexpr int kTileKBytes = kTileKeys * kRowBytes;
+constexpr int kTileLds = kTileKBytes + kTileKeys * kVRowBytes;              // 36 KB
+constexpr int kWaveKBytes = kStepKeys * kRowBytes;
+constexpr int kWaveLds = kWaveKBytes + kStepKeys * kVRowBytes;              // 18 KB
+constexpr int kChunkLds = 4 * kWaveLds;                                     // 72 KB
 constexpr int kMergeLds = (4 * 32 * 2 + 2 * kHeadDim * 32) * 4 + 16;
 constexpr int kLdsBytes = kTileLds > kChunkLds ? (kTileLds > kMergeLds ? kTileLds : kMergeLds)
                                                : (kChunkLds > kMergeLds ? kChunkLds : kMergeLds);
+// the running max moves only when a block's max exceeds it by this much (log2 units)
+constexpr float kRescaleThreshold = 8.f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
@@ -102,12 +108,10 @@ __device__ __forceinline__ int acc_key(int j, int hi) { return 16 * (j >> 3) + 8
 // head-dim index (within a 32-wide block) held by output accumulator j of lane half hi
 __device__ __forceinline__ int acc_d(int j, int hi) { return 8 * (j >> 2) + 4 * hi + (j & 3); }
 
-// chunk permutation of LDS row `key` (depends on key % 16 only)
+// K blocks: 16-byte chunk c of row `key` is stored at slot c ^ swz(key)
+// (depends on key % 16 only), so 16 consecutive rows read at one chunk hit
+// 16 distinct bank groups.
 __device__ __forceinline__ int swz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
-// byte offset of 16-byte chunk `chunk` of row `key` in a swizzled block
-__device__ __forceinline__ int row_chunk(int key, int chunk) {
-  return key * kRowBytes + ((chunk ^ swz(key)) << 4);
-}
 
 template <typename T>
 __device__ __forceinline__ u32x4 ld16(const T* p) {
@@ -120,24 +124,27 @@ __device__ __forceinline__ void lds_st16(char* base, int off, u32x4 v) {
   *reinterpret_cast<u32x4*>(base + off) = v;
 }
 
-// V^T operand of one 32x32x16 MFMA: lane (d = l % 32, half hi = l / 32) gets
-// V[key0 + 8*hi + e][d0 + l % 32], e = 0..7, from a swizzled row-major block.
-// Two transpose reads, each serving 4 keys x 16 dims per 16-lane group.
+// V^T operand of one 32x32x16 MFMA from a padded row-major V block: lane
+// (d = l % 32, half hi = l / 32) gets V[key0 + 8*hi + e][d0 + l % 32], e = 0..7.
+// Each ds_read_b64_tr_b16 serves 4 keys x 16 dims per 16-lane group; `vlane`
+// is the lane's constant part of the address (see vt_lane), the rest folds into
+// the instruction offset.
 template <typename V8>
-__device__ __forceinline__ V8 vt_operand(const char* blk, int key0, int d0, int lane) {
-  const int g = lane >> 4, i = lane & 15;
-  const int dchunk = (d0 >> 3) + 2 * (g & 1) + ((i & 3) >> 1);
-  const int half = 8 * (i & 1);
+__device__ __forceinline__ V8 vt_operand(const char* vlane, int key0, int d0) {
   u32x2 part[2];
 #pragma unroll
   for (int ld = 0; ld < 2; ++ld) {
-    const int key = key0 + 8 * (g >> 1) + 4 * ld + (i >> 2);
-    const LDS_AS char* p = (const LDS_AS char*)blk + row_chunk(key, dchunk) + half;
+    const LDS_AS char* p = (const LDS_AS char*)vlane + (key0 + 4 * ld) * kVRowBytes + d0 * 2;
     i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)p);
     part[ld] = __builtin_bit_cast(u32x2, v);
   }
   u32x4 w = {part[0][0], part[0][1], part[1][0], part[1][1]};
   return __builtin_bit_cast(V8, w);
+}
+// lane-dependent byte offset for vt_operand: row 8*(g/2) + i/4, dims 16*(g%2) + 4*(i%4)
+__device__ __forceinline__ int vt_lane(int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  return (8 * (g >> 1) + (i >> 2)) * kVRowBytes + (16 * (g & 1) + 4 * (i & 3)) * 2;
 }
 
 struct RowGeom {
@@ -147,9 +154,9 @@ struct RowGeom {
 struct RoleView {
   const void* q;
   int64_t q_st, q_sh;
-  const void* k;
-  const void* v;
-  int64_t kv_sp, kv_st, kv_sh;
+  const char* k;            // pool base + this item's kv head offset
+  const char* v;
+  uint32_t kv_sp_b, kv_st_b;
   const int32_t* indices;
   void* out;
   int64_t o_st, o_sh;
@@ -158,18 +165,18 @@ struct RoleView {
   int causal, window_left;
 };
 
-__device__ __forceinline__ RoleView pick_role(const Params& p, int role) {
+__device__ __forceinline__ RoleView pick_role(const Params& p, int role, int kvh) {
   const RoleParams& a = p.role[0];
   const RoleParams& b = p.role[1];
   RoleView r;
   r.q = role ? b.q : a.q;
   r.q_st = role ? b.q_st : a.q_st;
   r.q_sh = role ? b.q_sh : a.q_sh;
-  r.k = role ? b.k : a.k;
-  r.v = role ? b.v : a.v;
-  r.kv_sp = role ? b.kv_sp : a.kv_sp;
-  r.kv_st = role ? b.kv_st : a.kv_st;
-  r.kv_sh = role ? b.kv_sh : a.kv_sh;
+  const uint32_t sh = role ? b.kv_sh_b : a.kv_sh_b;
+  r.k = reinterpret_cast<const char*>(role ? b.k : a.k) + (uint64_t)kvh * sh;
+  r.v = reinterpret_cast<const char*>(role ? b.v : a.v) + (uint64_t)kvh * sh;
+  r.kv_sp_b = role ? b.kv_sp_b : a.kv_sp_b;
+  r.kv_st_b = role ? b.kv_st_b : a.kv_st_b;
   r.indices = role ? b.indices : a.indices;
   r.out = role ? b.out : a.out;
   r.o_st = role ? b.o_st : a.o_st;
@@ -181,19 +188,14 @@ __device__ __forceinline__ RoleView pick_role(const Params& p, int role) {
   return r;
 }
 
-// Element offset of (logical key, kv head) in a role's pool.
-__device__ __forceinline__ int64_t kv_offset(const RoleView& r, const Params& p, int page_start,
-                                             int key, int kvh) {
-  int pg, slot;
-  if (p.page_shift >= 0) {
-    pg = key >> p.page_shift;
-    slot = key & (p.page_size - 1);
-  } else {
-    pg = key / p.page_size;
-    slot = key - pg * p.page_size;
-  }
-  const int64_t page = r.indices ? (int64_t)r.indices[page_start + pg] : (int64_t)(page_start + pg);
-  return page * r.kv_sp + (int64_t)slot * r.kv_st + (int64_t)kvh * r.kv_sh;
+// Physical page of logical key `key` and the byte offset of its row in the pool.
+__device__ __forceinline__ uint32_t page_of(const RoleView& r, const Params& p, int page_start, int key) {
+  const int pg = p.page_shift >= 0 ? (key >> p.page_shift) : key / p.page_size;
+  return r.indices ? (uint32_t)r.indices[page_start + pg] : (uint32_t)(page_start + pg);
+}
+__device__ __forceinline__ uint64_t row_off(const RoleView& r, const Params& p, uint32_t page, int key) {
+  const int slot = p.page_shift >= 0 ? (key & (p.page_size - 1)) : key % p.page_size;
+  return (uint64_t)page * r.kv_sp_b + (uint32_t)slot * r.kv_st_b;
 }
 
 // Q^T operand of one row: lane half hi holds d = hi*64 + c*8 + [0,8) for MFMA c.
@@ -209,8 +211,28 @@ __device__ __forceinline__ void load_q(typename Dt<T>::v8 (&qreg)[8], const Role
   }
 }
 
+// Row range of the mask in "offset, span" form: key k is valid iff
+// (unsigned)(k - lo) <= span. Empty ranges never match.
+struct RowMask {
+  int lo;
+  unsigned span;
+};
+__device__ __forceinline__ RowMask row_mask(int key_lo, int key_hi) {
+  RowMask m;
+  if (key_hi < key_lo) {
+    m.lo = 1 << 30;
+    m.span = 0;
+  } else {
+    m.lo = key_lo;
+    m.span = (unsigned)(key_hi - key_lo);
+  }
+  return m;
+}
+
 // Online-softmax update for NB score blocks of one lane (raw scores, masked
-// entries already -inf). m is kept in raw units; returns P as MFMA operands.
+// entries already -inf). The running max m is in raw units and only moves when
+// a block max exceeds it by kRescaleThreshold (log2 units), so P stays below
+// 2^threshold and O is rescaled rarely. Returns P as MFMA operands.
 template <typename T, int NB>
 __device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float sl2, float& m, float& l,
                                              f32x16 (&o)[4], typename Dt<T>::v8 (&pb)[NB][2]) {
@@ -220,17 +242,18 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float sl2, float& 
 #pragma unroll
     for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[b][j]);
   mx = xhalf_max(mx);
-  const float mn = fmaxf(m, mx);
-  const float mu2 = (mn == kNegInf) ? 0.f : mn * sl2;
-  const float alpha = fast_exp2(m * sl2 - mu2);
-  if (__any(alpha != 1.f)) {
+  const bool upd = (m == kNegInf) ? (mx != kNegInf) : ((mx - m) * sl2 > kRescaleThreshold);
+  if (__any(upd)) {
+    const float mn = upd ? mx : m;
+    const float alpha = upd ? fast_exp2((m - mn) * sl2) : 1.f;
     l *= alpha;
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
+    m = mn;
   }
-  m = mn;
+  const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -264,26 +287,25 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   load_q<T>(qreg, r, row_ok, rg.qo_start + tok, head, hi);
 
   const int pdiag = rg.kv_len - rg.qo_len + tok;
-  const int key_hi = r.causal ? pdiag : rg.kv_len - 1;
+  const int key_hi = min(r.causal ? pdiag : rg.kv_len - 1, kv_end - 1);
   const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
+  const RowMask rm = row_mask(key_lo, key_hi);
 
   char* Ks = smem;
-  char* Vs = smem + kTileKeys * kRowBytes;
-  const T* kbase = reinterpret_cast<const T*>(r.k);
-  const T* vbase = reinterpret_cast<const T*>(r.v);
+  char* Vs = smem + kTileKBytes;
 
-  // staging: thread t moves rows (t >> 4) + 16 i, chunk slot t & 15
+  // staging: thread t moves rows (t >> 4) + 16 i, 16-byte slot t & 15
   const int st_key = threadIdx.x >> 4, st_slot = threadIdx.x & 15;
+  const int k_gchunk = (st_slot ^ swz(st_key)) << 4;   // K: global chunk for LDS slot st_slot
   u32x4 kst[4], vst[4];
   auto load_block = [&](int kb) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int key = st_key + 16 * i;
-      const int kidx = kb + key;
-      if (kidx < kv_end) {
-        const int64_t off = kv_offset(r, p, rg.page_start, kidx, kvh) + ((st_slot ^ swz(key)) << 3);
-        kst[i] = ld16(kbase + off);
-        vst[i] = ld16(vbase + off);
+      const int key = kb + st_key + 16 * i;
+      if (key < kv_end) {
+        const uint64_t off = row_off(r, p, page_of(r, p, rg.page_start, key), key);
+        kst[i] = ld16(r.k + off + k_gchunk);
+        vst[i] = ld16(r.v + off + (st_slot << 4));
       } else {
         kst[i] = u32x4{0, 0, 0, 0};
         vst[i] = u32x4{0, 0, 0, 0};
@@ -293,17 +315,17 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   auto store_block = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int off = (st_key + 16 * i) * kRowBytes + (st_slot << 4);
-      lds_st16(Ks, off, kst[i]);
-      lds_st16(Vs, off, vst[i]);
+      lds_st16(Ks, (st_key + 16 * i) * kRowBytes + (st_slot << 4), kst[i]);
+      lds_st16(Vs, (st_key + 16 * i) * kVRowBytes + (st_slot << 4), vst[i]);
     }
   };
 
-  // K operand offsets: lane reads row key_row(r32) (+32 h), chunk hi*8 + c
+  // K operand: lane reads row key_row(r32) (+32 h), chunk hi*8 + c
   const int krow = key_row(r32);
   int koff[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) koff[c] = row_chunk(krow, hi * 8 + c);
+  for (int c = 0; c < 8; ++c) koff[c] = krow * kRowBytes + (((hi * 8 + c) ^ swz(krow)) << 4);
+  const char* vlane = Vs + vt_lane(lane);
 
   f32x16 o[4];
 #pragma unroll
@@ -329,16 +351,13 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
         s[h] = Dt<T>::mfma(__builtin_bit_cast(V8, lds_ld16(Ks, h * 32 * kRowBytes + koff[c])),
                            qreg[c], s[h]);
     }
-    const bool need_mask =
-        __any(kb < key_lo || kb + kTileKeys - 1 > key_hi || kb + kTileKeys > kv_end);
-    if (need_mask) {
+    if (__any((unsigned)(kb - rm.lo) > rm.span || (unsigned)(kb + kTileKeys - 1 - rm.lo) > rm.span)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int kidx = kb + h * 32 + acc_key(j, hi);
-          const bool ok = kidx >= key_lo && kidx <= key_hi && kidx < kv_end;
-          s[h][j] = ok ? s[h][j] : kNegInf;
+          s[h][j] = ((unsigned)(kidx - rm.lo) <= rm.span) ? s[h][j] : kNegInf;
         }
     }
     V8 pb[2][2];
@@ -349,7 +368,7 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
       for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
         for (int db = 0; db < 4; ++db)
-          o[db] = Dt<T>::mfma(vt_operand<V8>(Vs, h * 32 + 16 * mp, db * 32, lane), pb[h][mp], o[db]);
+          o[db] = Dt<T>::mfma(vt_operand<V8>(vlane, h * 32 + 16 * mp, db * 32), pb[h][mp], o[db]);
 
     if (has_next) {
       __syncthreads();
@@ -383,11 +402,11 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
 
 // ----------------------------------------------------------------------------
 // Key chunk: all q_len x group rows (<= 32) of one request and kv head over keys
-// [kv_begin, kv_end). Wave w takes 32-key steps w, w+4, ... Lane (r, hi) loads
-// K and V of key key_row(r) of the step (its own 128 contiguous bytes of each):
-// K stays in registers as the MFMA A operand, V goes to the wave's LDS block
-// for the transpose reads. The next step's K/V loads are in flight while the
-// current step computes, and the page index is fetched one step further ahead.
+// [kv_begin, kv_end). Wave w takes 32-key steps w, w+4, ... Each wave load
+// instruction covers 4 whole 256-byte rows (16 lanes per row); K and V go to
+// the wave's own LDS blocks, from which the K operand and the V^T operand are
+// read. The next step's rows are in flight while the current step computes,
+// and the page indices are fetched one step further ahead.
 // Wave states merge in LDS; split chunks merge through the float workspace.
 template <typename T>
 __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg, int kvh,
@@ -405,72 +424,82 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   load_q<T>(qreg, r, row_ok, rg.qo_start + tok, head, hi);
 
   const int pdiag = rg.kv_len - rg.qo_len + tok;
-  const int key_hi = r.causal ? pdiag : rg.kv_len - 1;
+  const int key_hi = min(r.causal ? pdiag : rg.kv_len - 1, kv_end - 1);
   const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
+  const RowMask rm = row_mask(key_lo, key_hi);
 
-  char* vblk = smem + wave * (kStepKeys * kRowBytes);
+  char* Kw = smem + wave * kWaveLds;
+  char* Vw = Kw + kWaveKBytes;
   f32x16 o[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) o[b] = f32x16{};
   float m = kNegInf, l = 0.f;
   const float sl2 = r.scale_log2;
-  const int krow = key_row(r32);
-  const T* kbase = reinterpret_cast<const T*>(r.k);
-  const T* vbase = reinterpret_cast<const T*>(r.v);
-  int voff[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) voff[c] = row_chunk(krow, hi * 8 + c);
 
+  const int krow = key_row(r32);
+  int koff[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) koff[c] = krow * kRowBytes + (((hi * 8 + c) ^ swz(krow)) << 4);
+  const char* vlane = Vw + vt_lane(lane);
+
+  // loads: instruction i moves row 4 i + (lane >> 4) of the step, slot lane & 15
+  const int ld_row = lane >> 4, ld_slot = lane & 15;
   const int first = kv_begin + kStepKeys * wave;
   const int n_steps = first < kv_end ? (kv_end - first + 4 * kStepKeys - 1) / (4 * kStepKeys) : 0;
-  // element offset of this lane's key for step i, or -1 past the chunk
-  auto lane_off = [&](int i) -> int64_t {
-    const int key = first + 4 * kStepKeys * i + krow;
-    return key < kv_end ? kv_offset(r, p, rg.page_start, key, kvh) + hi * 64 : (int64_t)-1;
-  };
-  auto load_k = [&](u32x4 (&kx)[8], int64_t off) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) kx[c] = off >= 0 ? ld16(kbase + off + c * 8) : u32x4{0, 0, 0, 0};
-  };
-  auto load_v = [&](u32x4 (&vx)[8], int64_t off) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) vx[c] = off >= 0 ? ld16(vbase + off + c * 8) : u32x4{0, 0, 0, 0};
-  };
-
-  // K double-buffered in registers; V single-buffered (its registers are free
-  // again once the step's V is in LDS, before the next step's V is loaded)
-  u32x4 ka[8], kb_[8], vr[8];
-  int64_t off_next = -1;
-  if (n_steps > 0) {
-    const int64_t off0 = lane_off(0);
-    load_k(ka, off0);
-    load_v(vr, off0);
-    if (n_steps > 1) off_next = lane_off(1);
-  }
-
-  auto step = [&](int i, u32x4 (&kc)[8], u32x4 (&kn)[8]) {
+  uint32_t pidx[8];
+  u32x4 kst[8], vst[8];
+  auto load_pages = [&](int i) {
     const int kb = first + 4 * kStepKeys * i;
-    // V of this step to the wave's block; the previous step's reads of it are
-    // ordered before these writes (LDS executes a wave's requests in order)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) lds_st16(vblk, voff[c], vr[c]);
+    for (int c = 0; c < 8; ++c) {
+      const int key = kb + 4 * c + ld_row;
+      pidx[c] = key < kv_end ? page_of(r, p, rg.page_start, key) : 0u;
+    }
+  };
+  auto load_rows = [&](int i) {
+    const int kb = first + 4 * kStepKeys * i;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int key = kb + 4 * c + ld_row;
+      if (key < kv_end) {
+        const uint64_t off = row_off(r, p, pidx[c], key);
+        kst[c] = ld16(r.k + off + ((ld_slot ^ swz(4 * c + ld_row)) << 4));
+        vst[c] = ld16(r.v + off + (ld_slot << 4));
+      } else {
+        kst[c] = u32x4{0, 0, 0, 0};
+        vst[c] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+
+  if (n_steps > 0) {
+    load_pages(0);
+    load_rows(0);
+    if (n_steps > 1) load_pages(1);
+  }
+  for (int i = 0; i < n_steps; ++i) {
+    const int kb = first + 4 * kStepKeys * i;
+    // this step's rows to the wave's blocks; the previous step's reads of them
+    // are ordered before these writes (LDS runs a wave's requests in order)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      lds_st16(Kw, (4 * c + ld_row) * kRowBytes + (ld_slot << 4), kst[c]);
+      lds_st16(Vw, (4 * c + ld_row) * kVRowBytes + (ld_slot << 4), vst[c]);
+    }
     if (i + 1 < n_steps) {
-      load_k(kn, off_next);
-      load_v(vr, off_next);
-      off_next = (i + 2 < n_steps) ? lane_off(i + 2) : (int64_t)-1;
+      load_rows(i + 1);
+      if (i + 2 < n_steps) load_pages(i + 2);
     }
     f32x16 s[1];
     s[0] = f32x16{};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) s[0] = Dt<T>::mfma(__builtin_bit_cast(V8, kc[c]), qreg[c], s[0]);
-    const bool need_mask =
-        __any(kb < key_lo || kb + kStepKeys - 1 > key_hi || kb + kStepKeys > kv_end);
-    if (need_mask) {
+    for (int c = 0; c < 8; ++c)
+      s[0] = Dt<T>::mfma(__builtin_bit_cast(V8, lds_ld16(Kw, koff[c])), qreg[c], s[0]);
+    if (__any((unsigned)(kb - rm.lo) > rm.span || (unsigned)(kb + kStepKeys - 1 - rm.lo) > rm.span)) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int kidx = kb + acc_key(j, hi);
-        const bool ok = kidx >= key_lo && kidx <= key_hi && kidx < kv_end;
-        s[0][j] = ok ? s[0][j] : kNegInf;
+        s[0][j] = ((unsigned)(kidx - rm.lo) <= rm.span) ? s[0][j] : kNegInf;
       }
     }
     V8 pb[1][2];
@@ -479,11 +508,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
     for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        o[db] = Dt<T>::mfma(vt_operand<V8>(vblk, 16 * mp, db * 32, lane), pb[0][mp], o[db]);
-  };
-  for (int i = 0; i < n_steps; i += 2) {
-    step(i, ka, kb_);
-    if (i + 1 < n_steps) step(i + 1, kb_, ka);
+        o[db] = Dt<T>::mfma(vt_operand<V8>(vlane, 16 * mp, db * 32), pb[0][mp], o[db]);
   }
   l = xhalf_sum(l);
 
@@ -623,7 +648,7 @@ __global__ __launch_bounds__(kThreads, 2) void pod_grid_kernel(Params p) {
   const int role = flags & kFlagRole;
   const int req = it[1], kvh = it[2], tok0 = it[3], ntok = it[4];
   const int kv_begin = it[5], kv_end = it[6], grp = it[7];
-  const RoleView r = pick_role(p, role);
+  const RoleView r = pick_role(p, role, kvh);
   const int32_t* rq = p.reqs + req * kReqWords;
   RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
   if (flags & kFlagChunk)
