@@ -75,14 +75,21 @@ constexpr int kRowBytes = kHeadDim * 2;       // one kv head's K row (16-bit typ
 constexpr int kVRowBytes = kRowBytes + 64;    // V rows are padded by 64 bytes
 constexpr int kTileKeys = 64;                 // keys per LDS block of a query tile
 constexpr int kStepKeys = 32;                 // keys per wave step of a key chunk
-constexpr int kTileKBytes = kTileKeys * kRowBytes;
-constexpr int kTileLds = kTileKBytes + kTileKeys * kVRowBytes;              // 36 KB
+constexpr int kTileKBytes = kTileKeys * kRowBytes;                         // 16 KB
+// Query-tile V block: logical row R sits in 1088-byte group R % 16 at slot R / 16,
+// so each group is one lane-contiguous direct-to-LDS load of 4 rows and the 4
+// consecutive rows of a transpose read land 16 banks apart.
+constexpr int kTileVGroup = 4 * kRowBytes + 64;
+constexpr int kTileBuf = kTileKBytes + 16 * kTileVGroup;                    // 33 KB per buffer
 constexpr int kWaveKBytes = kStepKeys * kRowBytes;
 constexpr int kWaveLds = kWaveKBytes + kStepKeys * kVRowBytes;              // 18 KB
 constexpr int kChunkLds = 4 * kWaveLds;                                     // 72 KB
 constexpr int kMergeLds = (4 * 32 * 2 + 2 * kHeadDim * 32) * 4 + 16;
-constexpr int kLdsBytes = kTileLds > kChunkLds ? (kTileLds > kMergeLds ? kTileLds : kMergeLds)
-                                               : (kChunkLds > kMergeLds ? kChunkLds : kMergeLds);
+// two LDS arrays: the query tile double-buffers its K/V blocks across them, the
+// key chunk gives waves 0-1 the first and waves 2-3 the second
+constexpr int kLdsHalf = (kTileBuf > 2 * kWaveLds ? kTileBuf : 2 * kWaveLds) > kMergeLds
+                             ? (kTileBuf > 2 * kWaveLds ? kTileBuf : 2 * kWaveLds)
+                             : kMergeLds;
 // the running max moves only when a block's max exceeds it by this much (log2 units)
 constexpr float kRescaleThreshold = 8.f;
 
@@ -229,13 +236,13 @@ __device__ __forceinline__ RowMask row_mask(int key_lo, int key_hi) {
   return m;
 }
 
-// Online-softmax update for NB score blocks of one lane (raw scores, masked
-// entries already -inf). The running max m is in raw units and only moves when
-// a block max exceeds it by kRescaleThreshold (log2 units), so P stays below
-// 2^threshold and O is rescaled rarely. Returns P as MFMA operands.
-template <typename T, int NB>
-__device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float sl2, float& m, float& l,
-                                             f32x16 (&o)[4], typename Dt<T>::v8 (&pb)[NB][2]) {
+// Running-max update for NB score blocks of one lane (raw scores, masked
+// entries already -inf). m is kept in raw units and only moves when a block max
+// exceeds it by kRescaleThreshold (log2 units), so P stays below 2^threshold
+// and O and l are rescaled rarely.
+template <int NB>
+__device__ __forceinline__ void update_max(f32x16 (&s)[NB], float sl2, float& m, float& l,
+                                           f32x16 (&o)[4]) {
   float mx = kNegInf;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -253,26 +260,39 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float sl2, float& 
       for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
     m = mn;
   }
+}
+
+// P = exp2(s * sl2 - mu2) of one 32-key score block as two MFMA operands.
+template <typename T>
+__device__ __forceinline__ void exp_block(const f32x16& s, float sl2, float mu2, float& l,
+                                          typename Dt<T>::v8 (&pb)[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float e = fast_exp2(fmaf(s[8 * h + i], sl2, -mu2));
+      l += e;
+      pb[h][i] = (T)e;
+    }
+}
+
+template <typename T, int NB>
+__device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float sl2, float& m, float& l,
+                                             f32x16 (&o)[4], typename Dt<T>::v8 (&pb)[NB][2]) {
+  update_max<NB>(s, sl2, m, l, o);
   const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e = fast_exp2(fmaf(s[b][8 * h + i], sl2, -mu2));
-        l += e;
-        pb[b][h][i] = (T)e;
-      }
+  for (int b = 0; b < NB; ++b) exp_block<T>(s[b], sl2, mu2, l, pb[b]);
 }
 
 // ----------------------------------------------------------------------------
 // Query tile: up to 128 rows (tokens x group heads) of one request and kv head,
-// keys [kv_begin, kv_end) in 64-key blocks staged in LDS. The next block's
-// global loads are issued before the current block's MFMA work.
+// keys [kv_begin, kv_end) in 64-key blocks. K/V blocks go straight from HBM/L2
+// to LDS (16-byte direct loads) into two alternating buffers: the next block
+// streams in while the current one is computed, with one barrier per block.
 template <typename T>
 __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg, int kvh, int tok0,
-                          int ntok, int kv_begin, int kv_end, char* smem) {
+                          int ntok, int kv_begin, int kv_end, char* bufA, char* bufB) {
   using V8 = typename Dt<T>::v8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
@@ -291,41 +311,47 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
   const RowMask rm = row_mask(key_lo, key_hi);
 
-  char* Ks = smem;
-  char* Vs = smem + kTileKBytes;
-
-  // staging: thread t moves rows (t >> 4) + 16 i, 16-byte slot t & 15
-  const int st_key = threadIdx.x >> 4, st_slot = threadIdx.x & 15;
-  const int k_gchunk = (st_slot ^ swz(st_key)) << 4;   // K: global chunk for LDS slot st_slot
-  u32x4 kst[4], vst[4];
-  auto load_block = [&](int kb) {
+  // Direct loads: wave w issues groups 4w+u (u = 0..3) of both K and V; group i
+  // holds rows i + 16 (lane/16), lane & 15 is the 16-byte slot. K row R sits at
+  // (R % 16) * 1024 + (R / 16) * 256 with XOR-swizzled chunks; V row R at
+  // (R % 16) * 1088 + (R / 16) * 256 (1088-byte groups: the 4 consecutive rows of
+  // a transpose read land 16 banks apart).
+  const int lq = lane >> 4, lslot = lane & 15;
+  int rr[4], kchunk[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kb + st_key + 16 * i;
-      if (key < kv_end) {
-        const uint64_t off = row_off(r, p, page_of(r, p, rg.page_start, key), key);
-        kst[i] = ld16(r.k + off + k_gchunk);
-        vst[i] = ld16(r.v + off + (st_slot << 4));
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
-      }
+  for (int u = 0; u < 4; ++u) {
+    rr[u] = 4 * wave + u + 16 * lq;
+    kchunk[u] = (lslot ^ swz(rr[u])) << 4;
+  }
+  uint32_t pg[4];
+  // Rows past kv_end repeat row kv_end - 1: finite values whose scores the
+  // mask sends to -inf, so they add exactly zero to O.
+  auto load_pages = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pg[u] = page_of(r, p, rg.page_start, min(kb + rr[u], kv_end - 1));
+  };
+  auto dma_block = [&](int kb, char* buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint64_t ro = row_off(r, p, pg[u], min(kb + rr[u], kv_end - 1));
+      __builtin_amdgcn_global_load_lds((const void*)(r.k + ro + kchunk[u]),
+                                       (LDS_AS void*)(buf + (4 * wave + u) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(r.v + ro + (lslot << 4)),
+                                       (LDS_AS void*)(buf + kTileKBytes + (4 * wave + u) * kTileVGroup),
+                                       16, 0, 0);
     }
   };
-  auto store_block = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lds_st16(Ks, (st_key + 16 * i) * kRowBytes + (st_slot << 4), kst[i]);
-      lds_st16(Vs, (st_key + 16 * i) * kVRowBytes + (st_slot << 4), vst[i]);
-    }
-  };
 
-  // K operand: lane reads row key_row(r32) (+32 h), chunk hi*8 + c
+  // K operand: lane reads row h*32 + key_row(r32), chunk hi*8 + c
   const int krow = key_row(r32);
   int koff[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) koff[c] = krow * kRowBytes + (((hi * 8 + c) ^ swz(krow)) << 4);
-  const char* vlane = Vs + vt_lane(lane);
+  for (int c = 0; c < 8; ++c)
+    koff[c] = (krow & 15) * 1024 + (krow >> 4) * kRowBytes + (((hi * 8 + c) ^ swz(krow)) << 4);
+  // V^T operand: lane rows 8(g/2) + i/4 (+4 ld), dims 16(g%2) + 4(i%4)
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vlane = kTileKBytes + (8 * (vg >> 1) + (vi >> 2)) * kTileVGroup +
+                    (16 * (vg & 1) + 4 * (vi & 3)) * 2;
 
   f32x16 o[4];
 #pragma unroll
@@ -333,24 +359,33 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   float m = kNegInf, l = 0.f;
   const float sl2 = r.scale_log2;
 
-  if (kv_begin < kv_end) {
-    load_block(kv_begin);
-    store_block();
-  }
-  __syncthreads();
-  for (int kb = kv_begin; kb < kv_end; kb += kTileKeys) {
-    const bool has_next = kb + kTileKeys < kv_end;
-    if (has_next) load_block(kb + kTileKeys);
-
+  // One 64-key block: S for both 32-key halves (K fragments read ahead of the
+  // MFMAs), one running-max decision, then P0 / PV0 / P1 / PV1 as one
+  // straight-line region so the exp work of one half overlaps the other
+  // half's MFMAs.
+  auto compute_block = [&](int kb, const char* buf) {
     f32x16 s[2];
+    u32x4 kf[2][8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      s[h] = f32x16{};
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) kf[h][c] = lds_ld16(buf, 2 * h * kRowBytes + koff[c]);
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        s[h] = Dt<T>::mfma(__builtin_bit_cast(V8, lds_ld16(Ks, h * 32 * kRowBytes + koff[c])),
-                           qreg[c], s[h]);
+        s[h] = Dt<T>::mfma(__builtin_bit_cast(V8, kf[h][c]), qreg[c], s[h]);
+    // keep 4 fragment reads in flight ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
     if (__any((unsigned)(kb - rm.lo) > rm.span || (unsigned)(kb + kTileKeys - 1 - rm.lo) > rm.span)) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -360,21 +395,57 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
           s[h][j] = ((unsigned)(kidx - rm.lo) <= rm.span) ? s[h][j] : kNegInf;
         }
     }
-    V8 pb[2][2];
-    softmax_step<T, 2>(s, sl2, m, l, o, pb);
+    update_max<2>(s, sl2, m, l, o);
+    const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
+    const char* vb = buf + vlane;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h) {
+      V8 pb[2];
+      exp_block<T>(s[h], sl2, mu2, l, pb);
 #pragma unroll
       for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-          o[db] = Dt<T>::mfma(vt_operand<V8>(vlane, h * 32 + 16 * mp, db * 32), pb[h][mp], o[db]);
-
-    if (has_next) {
-      __syncthreads();
-      store_block();
-      __syncthreads();
+        for (int db = 0; db < 4; ++db) {
+          // rows 32 h + 16 mp + [lane part] + 4 ld: slot-row 2 h + mp of the groups
+          u32x2 part[2];
+#pragma unroll
+          for (int ld = 0; ld < 2; ++ld) {
+            const LDS_AS char* pp = (const LDS_AS char*)vb + 4 * ld * kTileVGroup +
+                                    (2 * h + mp) * kRowBytes + db * 64;
+            part[ld] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)pp));
+          }
+          const u32x4 w = {part[0][0], part[0][1], part[1][0], part[1][1]};
+          o[db] = Dt<T>::mfma(__builtin_bit_cast(V8, w), pb[mp], o[db]);
+        }
     }
+  };
+
+  if (kv_begin < kv_end) {
+    load_pages(kv_begin);
+    dma_block(kv_begin, bufA);
+    if (kv_begin + kTileKeys < kv_end) load_pages(kv_begin + kTileKeys);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kb = kv_begin; kb < kv_end; kb += 2 * kTileKeys) {
+    // block kb in bufA
+    if (kb + kTileKeys < kv_end) {
+      dma_block(kb + kTileKeys, bufB);
+      if (kb + 2 * kTileKeys < kv_end) load_pages(kb + 2 * kTileKeys);
+    }
+    compute_block(kb, bufA);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int kb1 = kb + kTileKeys;
+    if (kb1 >= kv_end) break;
+    // block kb1 in bufB
+    if (kb1 + kTileKeys < kv_end) {
+      dma_block(kb1 + kTileKeys, bufA);
+      if (kb1 + 2 * kTileKeys < kv_end) load_pages(kb1 + 2 * kTileKeys);
+    }
+    compute_block(kb1, bufB);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
   l = xhalf_sum(l);
 
@@ -410,7 +481,7 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
 // Wave states merge in LDS; split chunks merge through the float workspace.
 template <typename T>
 __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg, int kvh,
-                           int kv_begin, int kv_end, int split, int grp, char* smem) {
+                           int kv_begin, int kv_end, int split, int grp, char* bufA, char* bufB) {
   using V8 = typename Dt<T>::v8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
@@ -428,7 +499,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
   const RowMask rm = row_mask(key_lo, key_hi);
 
-  char* Kw = smem + wave * kWaveLds;
+  char* Kw = (wave < 2 ? bufA : bufB) + (wave & 1) * kWaveLds;
   char* Vw = Kw + kWaveKBytes;
   f32x16 o[4];
 #pragma unroll
@@ -451,24 +522,17 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   auto load_pages = [&](int i) {
     const int kb = first + 4 * kStepKeys * i;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int key = kb + 4 * c + ld_row;
-      pidx[c] = key < kv_end ? page_of(r, p, rg.page_start, key) : 0u;
-    }
+    for (int c = 0; c < 8; ++c)
+      pidx[c] = page_of(r, p, rg.page_start, min(kb + 4 * c + ld_row, kv_end - 1));
   };
+  // rows past kv_end repeat row kv_end - 1 (masked to zero weight)
   auto load_rows = [&](int i) {
     const int kb = first + 4 * kStepKeys * i;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int key = kb + 4 * c + ld_row;
-      if (key < kv_end) {
-        const uint64_t off = row_off(r, p, pidx[c], key);
-        kst[c] = ld16(r.k + off + ((ld_slot ^ swz(4 * c + ld_row)) << 4));
-        vst[c] = ld16(r.v + off + (ld_slot << 4));
-      } else {
-        kst[c] = u32x4{0, 0, 0, 0};
-        vst[c] = u32x4{0, 0, 0, 0};
-      }
+      const uint64_t off = row_off(r, p, pidx[c], min(kb + 4 * c + ld_row, kv_end - 1));
+      kst[c] = ld16(r.k + off + ((ld_slot ^ swz(4 * c + ld_row)) << 4));
+      vst[c] = ld16(r.v + off + (ld_slot << 4));
     }
   };
 
@@ -514,7 +578,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
 
   // ---- merge the 4 wave states in LDS
   __syncthreads();
-  float* sm_m = reinterpret_cast<float*>(smem);   // [4][32]
+  float* sm_m = reinterpret_cast<float*>(bufA);   // [4][32]
   float* sm_l = sm_m + 128;                       // [4][32]
   float* accA = sm_l + 128;                       // [128 d][32 rows]
   float* accB = accA + kHeadDim * 32;
@@ -641,7 +705,8 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
 
 template <typename T>
 __global__ __launch_bounds__(kThreads, 2) void pod_grid_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(16))) char bufA[kLdsHalf];
+  __shared__ __attribute__((aligned(16))) char bufB[kLdsHalf];
   const int32_t* it = p.items + (int64_t)blockIdx.x * kItemWords;
   const int flags = it[0];
   if (flags < 0) return;
@@ -652,9 +717,9 @@ __global__ __launch_bounds__(kThreads, 2) void pod_grid_kernel(Params p) {
   const int32_t* rq = p.reqs + req * kReqWords;
   RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
   if (flags & kFlagChunk)
-    chunk_item<T>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, smem);
+    chunk_item<T>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, bufA, bufB);
   else
-    tile_item<T>(p, r, rg, kvh, tok0, ntok, kv_begin, kv_end, smem);
+    tile_item<T>(p, r, rg, kvh, tok0, ntok, kv_begin, kv_end, bufA, bufB);
 }
 
 }  // namespace
