@@ -22,8 +22,8 @@ namespace {
 
 struct Item {
   int32_t w[kItemWords];
-  double cost;
-  int xcd;
+  int64_t cost;
+  int32_t xcd;
 };
 
 struct Req {
@@ -39,12 +39,13 @@ int fail(std::string* err, int code, const std::string& msg) {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Relative cost estimates used only to order and place items. A query tile is
-// MFMA work proportional to padded rows x keys; a key chunk is HBM traffic
-// proportional to keys (K and V rows of one kv head). The constants put both
-// in microseconds per CU at a nominal fraction of MI355X peak.
-double tile_cost(int64_t keys) { return 128.0 * 4.0 * kHeadDim * (double)keys / 4.9e12 * 1e6; }
-double chunk_cost(int64_t keys) { return 2.0 * kHeadDim * 2.0 * (double)keys / 31.0e9 * 1e6; }
+// Relative cost estimates used only to order and place items, in integer
+// units of roughly a nanosecond per CU: a query tile is MFMA work proportional
+// to padded rows x keys (128 x 4 x 128 FLOP per key at ~4.9 TFLOP/s per CU), a
+// key chunk is HBM traffic proportional to keys (512 bytes per key at ~31 GB/s
+// per CU).
+constexpr int64_t kTileCostPerKey = 13;
+constexpr int64_t kChunkCostPerKey = 16;
 
 int validate_role(const pod_role_desc& r, const char* name, int page_size, std::string* err) {
   char buf[256];
@@ -158,17 +159,25 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
     C = std::max<int64_t>(256, round_up((chunk_keys_total + target - 1) / std::max<int64_t>(target, 1), 64));
   }
 
-  std::vector<Item> items;
+  // exact item count first, so the item array is allocated once
+  const int T = std::max(1, kTileRows / g);
+  size_t n_items_total = 0;
+  for (const Req& q : reqs) {
+    if (q.qo_len == 0) continue;
+    if (is_chunk(q)) n_items_total += (size_t)H * (size_t)((q.kv_len - chunk_lo(q) + C - 1) / C);
+    else n_items_total += (size_t)H * (size_t)((q.qo_len + T - 1) / T);
+  }
+  std::vector<Item> items(n_items_total);
   std::vector<int32_t> groups;  // n_groups x 4
   int32_t n_slots = 0;
+  size_t ni = 0;
   for (size_t ri = 0; ri < reqs.size(); ++ri) {
     const Req& q = reqs[ri];
     const pod_role_desc& r = *roles[q.role];
     if (q.qo_len == 0) continue;
     if (is_chunk(q)) {
-      int64_t lo = chunk_lo(q), hi = q.kv_len;
-      int64_t n = hi - lo;
-      int64_t splits = (n + C - 1) / C;
+      const int64_t lo = chunk_lo(q), hi = q.kv_len;
+      const int64_t splits = (hi - lo + C - 1) / C;
       for (int kvh = 0; kvh < H; ++kvh) {
         int32_t grp = -1;
         if (splits > 1) {
@@ -179,10 +188,10 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
           groups.push_back(kvh);
           n_slots += (int32_t)splits;
         }
-        for (int64_t s = 0; s < splits; ++s) {
-          Item it;
-          int64_t b0 = lo + s * C, b1 = std::min<int64_t>(hi, b0 + C);
-          it.w[0] = q.role | kFlagChunk | (int32_t)(s << kSplitShift);
+        for (int64_t sp = 0; sp < splits; ++sp) {
+          Item& it = items[ni++];
+          const int64_t b0 = lo + sp * C, b1 = std::min<int64_t>(hi, b0 + C);
+          it.w[0] = q.role | kFlagChunk | (int32_t)(sp << kSplitShift);
           it.w[1] = (int32_t)ri;
           it.w[2] = kvh;
           it.w[3] = 0;
@@ -190,20 +199,18 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
           it.w[5] = (int32_t)b0;
           it.w[6] = (int32_t)b1;
           it.w[7] = grp;
-          it.cost = chunk_cost(b1 - b0);
+          it.cost = kChunkCostPerKey * (b1 - b0);
           it.xcd = -1;
-          items.push_back(it);
         }
       }
     } else {
-      int T = std::max(1, kTileRows / g);
       for (int t0 = 0; t0 < q.qo_len; t0 += T) {
-        int ntok = std::min(T, q.qo_len - t0);
-        int64_t pf = (int64_t)q.kv_len - q.qo_len + t0, pl = pf + ntok - 1;
-        int64_t hi = r.causal ? pl + 1 : q.kv_len;
-        int64_t lo = r.window_left >= 0 ? std::max<int64_t>(0, pf - r.window_left) : 0;
+        const int ntok = std::min(T, q.qo_len - t0);
+        const int64_t pf = (int64_t)q.kv_len - q.qo_len + t0, pl = pf + ntok - 1;
+        const int64_t hi = r.causal ? pl + 1 : q.kv_len;
+        const int64_t lo = r.window_left >= 0 ? std::max<int64_t>(0, pf - r.window_left) : 0;
         for (int kvh = 0; kvh < H; ++kvh) {
-          Item it;
+          Item& it = items[ni++];
           it.w[0] = q.role;
           it.w[1] = (int32_t)ri;
           it.w[2] = kvh;
@@ -212,65 +219,71 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
           it.w[5] = (int32_t)lo;
           it.w[6] = (int32_t)hi;
           it.w[7] = -1;
-          it.cost = tile_cost(hi - lo);
+          it.cost = kTileCostPerKey * (hi - lo);
           // tiles sharing one request's K/V for one kv head stay on one die (L2 reuse)
-          it.xcd = (int)((ri * (size_t)H + kvh) % kNumXcds);
-          items.push_back(it);
+          it.xcd = (int32_t)((ri * (size_t)H + kvh) % kNumXcds);
         }
       }
     }
   }
 
-  // Place items on dies. Tiles keep their die; key chunks go to the least loaded
-  // die, heaviest first (LPT).
-  std::vector<double> load(kNumXcds, 0.0);
-  std::vector<size_t> order(items.size());
-  for (size_t i = 0; i < items.size(); ++i) order[i] = i;
-  std::stable_sort(order.begin(), order.end(),
-                   [&](size_t a, size_t b) { return items[a].cost > items[b].cost; });
-  for (size_t i : order)
-    if (items[i].xcd >= 0) load[items[i].xcd] += items[i].cost;
-  for (size_t i : order) {
-    if (items[i].xcd >= 0) continue;
-    int best = (int)(std::min_element(load.begin(), load.end()) - load.begin());
-    items[i].xcd = best;
-    load[best] += items[i].cost;
+  // Heaviest first: a stable counting sort on the cost quantised to 1024 levels.
+  int64_t max_cost = 1;
+  for (const Item& it : items) max_cost = std::max(max_cost, it.cost);
+  constexpr int kLevels = 1024;
+  std::vector<int32_t> bucket_start(kLevels + 1, 0);
+  std::vector<int16_t> level(items.size());
+  const double to_level = (double)(kLevels - 1) / (double)max_cost;
+  for (size_t i = 0; i < items.size(); ++i) {
+    // level 0 = heaviest
+    const int lv = std::min(kLevels - 1, (int)((double)(max_cost - items[i].cost) * to_level));
+    level[i] = (int16_t)lv;
+    ++bucket_start[lv + 1];
+  }
+  for (int b = 0; b < kLevels; ++b) bucket_start[b + 1] += bucket_start[b];
+  std::vector<uint32_t> order(items.size());
+  for (size_t i = 0; i < items.size(); ++i) order[bucket_start[level[i]]++] = (uint32_t)i;
+
+  // Place items on dies. Tiles keep their die; key chunks go to the least
+  // loaded die, heaviest first (LPT).
+  int64_t load[kNumXcds] = {};
+  for (const Item& it : items)
+    if (it.xcd >= 0) load[it.xcd] += it.cost;
+  for (uint32_t i : order) {
+    Item& it = items[i];
+    if (it.xcd >= 0) continue;
+    int best = 0;
+    for (int x = 1; x < kNumXcds; ++x)
+      if (load[x] < load[best]) best = x;
+    it.xcd = best;
+    load[best] += it.cost;
   }
 
-  // Per die: order by the policy. Each role's items run heaviest first;
-  // POD_ORDER_INTERLEAVE merges the two roles in proportion to their cost so
-  // both kinds are resident on every CU at once.
-  std::vector<std::vector<size_t>> per(kNumXcds);
-  for (size_t i : order) per[items[i].xcd].push_back(i);
-  size_t max_len = 0;
-  for (int x = 0; x < kNumXcds; ++x) {
-    std::vector<size_t> pre, dec;
-    for (size_t i : per[x]) ((items[i].w[0] & kFlagRole) ? dec : pre).push_back(i);
-    std::vector<size_t> out;
-    if (d.order == POD_ORDER_PREFILL_FIRST) {
-      out = pre;
-      out.insert(out.end(), dec.begin(), dec.end());
-    } else if (d.order == POD_ORDER_DECODE_FIRST) {
-      out = dec;
-      out.insert(out.end(), pre.begin(), pre.end());
-    } else {
-      double tp = 0, td = 0;
-      for (size_t i : pre) tp += items[i].cost;
-      for (size_t i : dec) td += items[i].cost;
-      double cp = 0, cd = 0;
-      size_t a = 0, b = 0;
-      while (a < pre.size() || b < dec.size()) {
-        bool take_pre;
-        if (a == pre.size()) take_pre = false;
-        else if (b == dec.size()) take_pre = true;
-        else take_pre = (cp / tp) <= (cd / td);
-        if (take_pre) { cp += items[pre[a]].cost; out.push_back(pre[a++]); }
-        else { cd += items[dec[b]].cost; out.push_back(dec[b++]); }
-      }
+  // Per die: each role's items heaviest first; POD_ORDER_INTERLEAVE merges the
+  // two roles in proportion to their cost so both kinds are resident on every
+  // CU at once.
+  std::vector<uint32_t> per_pre[kNumXcds], per_dec[kNumXcds];
+  int64_t tp[kNumXcds] = {}, td[kNumXcds] = {};
+  {
+    size_t np[kNumXcds] = {}, nd[kNumXcds] = {};
+    for (const Item& it : items) ++((it.w[0] & kFlagRole) ? nd : np)[it.xcd];
+    for (int x = 0; x < kNumXcds; ++x) {
+      per_pre[x].reserve(np[x]);
+      per_dec[x].reserve(nd[x]);
     }
-    per[x] = out;
-    max_len = std::max(max_len, out.size());
   }
+  for (uint32_t i : order) {
+    const Item& it = items[i];
+    if (it.w[0] & kFlagRole) {
+      per_dec[it.xcd].push_back(i);
+      td[it.xcd] += it.cost;
+    } else {
+      per_pre[it.xcd].push_back(i);
+      tp[it.xcd] += it.cost;
+    }
+  }
+  size_t max_len = 0;
+  for (int x = 0; x < kNumXcds; ++x) max_len = std::max(max_len, per_pre[x].size() + per_dec[x].size());
 
   const int64_t grid = (int64_t)max_len * kNumXcds;
   const int n_groups = (int)(groups.size() / kGroupWords);
@@ -282,8 +295,9 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   if (grid > INT32_MAX / 2 || total > INT32_MAX / 2)
     return fail(err, POD_ERR_UNSUPPORTED, "plan too large");
 
-  image.assign((size_t)total, 0);
+  image.resize((size_t)total);
   int32_t* h = image.data();
+  std::fill(h, h + POD_HDR_WORDS, 0);
   h[0] = POD_IMAGE_MAGIC;
   h[1] = (int32_t)items.size();
   h[2] = (int32_t)grid;
@@ -297,27 +311,40 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   h[10] = kSlotFloats;
   h[11] = (int32_t)std::min<int64_t>(C, INT32_MAX);
   for (size_t i = 0; i < reqs.size(); ++i) {
-    int32_t* p = h + reqs_off + i * kReqWords;
-    p[0] = reqs[i].qo_start;
-    p[1] = reqs[i].qo_len;
-    p[2] = reqs[i].kv_len;
-    p[3] = reqs[i].page_start;
-  }
-  for (int64_t s = 0; s < grid; ++s) {
-    int32_t* p = h + items_off + s * kItemWords;
-    for (int k = 0; k < kItemWords; ++k) p[k] = 0;
-    p[0] = -1;
+    int32_t* q = h + reqs_off + i * kReqWords;
+    q[0] = reqs[i].qo_start;
+    q[1] = reqs[i].qo_len;
+    q[2] = reqs[i].kv_len;
+    q[3] = reqs[i].page_start;
   }
   int n_pre = 0, n_dec = 0;
   for (int x = 0; x < kNumXcds; ++x) {
-    for (size_t k = 0; k < per[x].size(); ++k) {
-      const Item& it = items[per[x][k]];
-      int32_t* p = h + items_off + ((int64_t)k * kNumXcds + x) * kItemWords;
-      for (int j = 0; j < kItemWords; ++j) p[j] = it.w[j];
-      if (it.w[0] & kFlagRole) ++n_dec; else ++n_pre;
+    const std::vector<uint32_t>& pre = per_pre[x];
+    const std::vector<uint32_t>& dec = per_dec[x];
+    size_t a = 0, b = 0, k = 0;
+    int64_t cp = 0, cd = 0;
+    while (a < pre.size() || b < dec.size()) {
+      bool take_pre;
+      if (a == pre.size()) take_pre = false;
+      else if (b == dec.size()) take_pre = true;
+      else if (d.order == POD_ORDER_PREFILL_FIRST) take_pre = true;
+      else if (d.order == POD_ORDER_DECODE_FIRST) take_pre = false;
+      else take_pre = cp * td[x] <= cd * tp[x];   // cp/tp <= cd/td
+      const Item& it = items[take_pre ? pre[a] : dec[b]];
+      if (take_pre) { cp += it.cost; ++a; ++n_pre; }
+      else { cd += it.cost; ++b; ++n_dec; }
+      int32_t* w = h + items_off + ((int64_t)k * kNumXcds + x) * kItemWords;
+      for (int j = 0; j < kItemWords; ++j) w[j] = it.w[j];
+      ++k;
+    }
+    for (; k < max_len; ++k) {   // idle slots
+      int32_t* w = h + items_off + ((int64_t)k * kNumXcds + x) * kItemWords;
+      w[0] = -1;
+      for (int j = 1; j < kItemWords; ++j) w[j] = 0;
     }
   }
   for (int i = 0; i < n_groups * kGroupWords; ++i) h[groups_off + i] = groups[i];
+  for (int i = 0; i < n_groups; ++i) h[counters_off + i] = 0;
 
   info.n_items = (int32_t)items.size();
   info.n_prefill_items = n_pre;
