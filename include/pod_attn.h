@@ -49,7 +49,12 @@ enum {
 enum { POD_DTYPE_F16 = 0, POD_DTYPE_BF16 = 1 };
 
 /* Item order policies for the fused grid (see pod_plan_desc.order). */
-enum { POD_ORDER_INTERLEAVE = 0, POD_ORDER_PREFILL_FIRST = 1, POD_ORDER_DECODE_FIRST = 2 };
+enum {
+  POD_ORDER_INTERLEAVE = 0,
+  POD_ORDER_PREFILL_FIRST = 1,
+  POD_ORDER_DECODE_FIRST = 2,
+  POD_ORDER_LONGEST_FIRST = 3
+};
 
 /*
  * One role of the POD call ([POD] "批量 POD" plan inputs: qo_indptr, kv_indptr,
@@ -95,7 +100,11 @@ typedef struct pod_role_desc {
  *                 (pod_plan_compute / pod_workspace_bytes).
  *   decode_chunk  keys per split of a decode request: 0 = planner's choice,
  *                 -1 = never split, else rounded up to a multiple of 64.
- *   order         POD_ORDER_* policy for how prefill and decode items share the grid.
+ *   order         POD_ORDER_* policy for how prefill and decode items share the grid:
+ *                 INTERLEAVE (default) mixes them in proportion to their estimated
+ *                 cost, decode slightly ahead; PREFILL_FIRST / DECODE_FIRST run one
+ *                 role's items before the other's; LONGEST_FIRST takes the items of
+ *                 both roles heaviest first. Any other value is POD_ERR_INVALID.
  */
 typedef struct pod_plan_desc {
   pod_role_desc prefill;

@@ -24,6 +24,7 @@ POD_DTYPE_BF16 = 1
 POD_ORDER_INTERLEAVE = 0
 POD_ORDER_PREFILL_FIRST = 1
 POD_ORDER_DECODE_FIRST = 2
+POD_ORDER_LONGEST_FIRST = 3
 
 POD_HDR_WORDS = 16
 POD_IMAGE_MAGIC = 0x504F4431

@@ -40,12 +40,16 @@ int fail(std::string* err, int code, const std::string& msg) {
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Relative cost estimates used only to order and place items, in integer
-// units of roughly a nanosecond per CU: a query tile is MFMA work proportional
-// to padded rows x keys (128 x 4 x 128 FLOP per key at ~4.9 TFLOP/s per CU), a
-// key chunk is HBM traffic proportional to keys (512 bytes per key at ~31 GB/s
-// per CU).
-constexpr int64_t kTileCostPerKey = 13;
-constexpr int64_t kChunkCostPerKey = 16;
+// units of roughly a nanosecond of one workgroup slot: a query tile costs
+// ~40 ns per key (128 rows x 64-key blocks at ~2.5 us per block), a key chunk
+// ~26 ns per key (512 bytes per key, with the HBM shared by the chunks that
+// run beside the tiles). Measured per item on MI355X.
+constexpr int64_t kTileCostPerKey = 40;
+constexpr int64_t kChunkCostPerKey = 26;
+// POD_ORDER_INTERLEAVE places decode items ahead of their cost share by this
+// factor, so the decode work (whose items are all of similar size) is done
+// at ~80% of each die's list and the lightest query tiles fill the tail.
+constexpr double kDecodeLead = 1.25;
 
 int validate_role(const pod_role_desc& r, const char* name, int page_size, std::string* err) {
   char buf[256];
@@ -110,7 +114,7 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   if (d.page_size < 1) return fail(err, POD_ERR_INVALID, "page_size must be >= 1");
   if (d.dtype != POD_DTYPE_F16 && d.dtype != POD_DTYPE_BF16)
     return fail(err, POD_ERR_UNSUPPORTED, "dtype must be POD_DTYPE_F16 or POD_DTYPE_BF16");
-  if (d.order < 0 || d.order > 2) return fail(err, POD_ERR_INVALID, "unknown order policy");
+  if (d.order < 0 || d.order > 3) return fail(err, POD_ERR_INVALID, "unknown order policy");
   const int g = d.num_qo_heads / d.num_kv_heads;
   if (g > kTileRows) return fail(err, POD_ERR_UNSUPPORTED, "group size above 128 is not supported");
   int rc = validate_role(d.prefill, "prefill", d.page_size, err);
@@ -261,7 +265,8 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
 
   // Per die: each role's items heaviest first; POD_ORDER_INTERLEAVE merges the
   // two roles in proportion to their cost so both kinds are resident on every
-  // CU at once.
+  // CU at once (the HBM-bound decode items then never all run together), and
+  // POD_ORDER_LONGEST_FIRST merges them heaviest first.
   std::vector<uint32_t> per_pre[kNumXcds], per_dec[kNumXcds];
   int64_t tp[kNumXcds] = {}, td[kNumXcds] = {};
   {
@@ -329,7 +334,9 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
       else if (b == dec.size()) take_pre = true;
       else if (d.order == POD_ORDER_PREFILL_FIRST) take_pre = true;
       else if (d.order == POD_ORDER_DECODE_FIRST) take_pre = false;
-      else take_pre = cp * td[x] <= cd * tp[x];   // cp/tp <= cd/td
+      else if (d.order == POD_ORDER_LONGEST_FIRST) take_pre = items[pre[a]].cost >= items[dec[b]].cost;
+      else   // cp/tp <= kDecodeLead * cd/td: decode runs ahead of its cost share
+        take_pre = (double)cp * (double)td[x] <= kDecodeLead * (double)cd * (double)tp[x];
       const Item& it = items[take_pre ? pre[a] : dec[b]];
       if (take_pre) { cp += it.cost; ++a; ++n_pre; }
       else { cd += it.cost; ++b; ++n_dec; }

@@ -151,7 +151,7 @@ def test_auto_split_gives_enough_items_for_single_decode():
 
 def test_orders_are_permutations_of_the_same_items():
     base = None
-    for order in (0, 1, 2):
+    for order in (0, 1, 2, 3):
         desc, keep = plan_desc(prefill=dict(qo_lens=[100, 50], kv_lens=[100, 60]),
                                decode=dict(qo_lens=[1] * 9, kv_lens=list(range(100, 1000, 100))),
                                hqo=8, hkv=2, order=order)
@@ -160,6 +160,21 @@ def test_orders_are_permutations_of_the_same_items():
         items = sorted(tuple(int(x) for x in it[1:7]) for it in im["items"] if it[0] != -1)
         base = base or items
         assert items == base
+
+
+def test_longest_first_orders_each_die_by_estimated_cost():
+    # the planner's estimates: 40 units per key of a query tile, 26 per key of a key chunk
+    desc, keep = plan_desc(prefill=dict(qo_lens=[300, 50], kv_lens=[700, 60]),
+                           decode=dict(qo_lens=[1] * 9, kv_lens=list(range(100, 1000, 100))),
+                           hqo=8, hkv=2, order=3, decode_chunk=-1)
+    rc, img, info = compute(desc)
+    im = decode_image(img)
+    items = im["items"]
+    grid = len(items)
+    for x in range(8):
+        costs = [(26 if int(it[0]) & FLAG_CHUNK else 40) * int(it[6] - it[5])
+                 for it in items[x::8] if it[0] != -1]
+        assert costs == sorted(costs, reverse=True)
 
 
 def test_workspace_sizes():
