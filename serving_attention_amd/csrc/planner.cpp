@@ -116,7 +116,7 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
     return fail(err, POD_ERR_UNSUPPORTED, "dtype must be POD_DTYPE_F16 or POD_DTYPE_BF16");
   if (d.order < 0 || d.order > 3) return fail(err, POD_ERR_INVALID, "unknown order policy");
   const int g = d.num_qo_heads / d.num_kv_heads;
-  if (g > kTileRows) return fail(err, POD_ERR_UNSUPPORTED, "group size above 128 is not supported");
+  if (g > kMaxGroup) return fail(err, POD_ERR_UNSUPPORTED, "group size above 128 is not supported");
   int rc = validate_role(d.prefill, "prefill", d.page_size, err);
   if (rc) return rc;
   rc = validate_role(d.decode, "decode", d.page_size, err);

@@ -10,8 +10,9 @@
 namespace pod {
 
 constexpr int kHeadDim = 128;
-constexpr int kThreads = 256;          // 4 wave64 per workgroup
-constexpr int kTileRows = 128;         // rows of a query-tile item (4 waves x 32)
+constexpr int kThreads = 512;          // 8 wave64 per workgroup (2 per SIMD)
+constexpr int kTileRows = 256;         // rows of a query-tile item (8 waves x 32)
+constexpr int kMaxGroup = 128;         // largest supported num_qo_heads / num_kv_heads
 constexpr int kChunkRows = 32;         // max rows of a key-chunk item (one MFMA column block)
 constexpr int kItemWords = 8;
 constexpr int kReqWords = 4;

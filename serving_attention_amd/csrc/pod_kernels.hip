@@ -83,13 +83,15 @@ constexpr int kTileVGroup = 4 * kRowBytes + 64;
 constexpr int kTileBuf = kTileKBytes + 16 * kTileVGroup;                    // 33 KB per buffer
 constexpr int kWaveKBytes = kStepKeys * kRowBytes;
 constexpr int kWaveLds = kWaveKBytes + kStepKeys * kVRowBytes;              // 18 KB
-constexpr int kChunkLds = 4 * kWaveLds;                                     // 72 KB
-constexpr int kMergeLds = (4 * 32 * 2 + 2 * kHeadDim * 32) * 4 + 16;
-// two LDS arrays: the query tile double-buffers its K/V blocks across them, the
-// key chunk gives waves 0-1 the first and waves 2-3 the second
-constexpr int kLdsHalf = (kTileBuf > 2 * kWaveLds ? kTileBuf : 2 * kWaveLds) > kMergeLds
-                             ? (kTileBuf > 2 * kWaveLds ? kTileBuf : 2 * kWaveLds)
-                             : kMergeLds;
+constexpr int kWaves = kThreads / 64;                                      // 8 waves
+constexpr int kRingSlots = 4;                                               // query-tile ring
+constexpr int kIdSlot = kWaves * 256;                                       // page ids, one ring slot
+// merge of the key-chunk waves: maxima and sums of 8 waves, 4 partial O sums
+constexpr int kMergeLds = (2 * kWaves * 32 + 4 * kHeadDim * 32) * 4 + 16;
+constexpr int kMax2(int a, int b) { return a > b ? a : b; }
+// one LDS array: the query tile's ring slots, or one 18 KB part per key-chunk wave
+constexpr int kLdsMain = kMax2(kMax2(kRingSlots * kTileBuf, kWaves * kWaveLds), kMergeLds);
+static_assert(kLdsMain + kRingSlots * kIdSlot <= 160 * 1024, "LDS budget");
 // the running max moves only when a block's max exceeds it by this much (log2 units)
 constexpr float kRescaleThreshold = 8.f;
 
@@ -119,6 +121,35 @@ __device__ __forceinline__ int acc_d(int j, int hi) { return 8 * (j >> 2) + 4 * 
 // (depends on key % 16 only), so 16 consecutive rows read at one chunk hit
 // 16 distinct bank groups.
 __device__ __forceinline__ int swz(int key) { return ((key & 3) << 2) | ((key >> 2) & 3); }
+
+// The query tile's direct-to-LDS ring is managed by hand: its loads are
+// issued through inline asm, so the compiler neither tracks them nor adds
+// waits of its own (compiler-tracked loads lose track of which LDS slot each
+// one targets across the loop back edge and then drain every outstanding
+// load), and the ring waits with explicit vmcnt counts.
+//
+// One 16-byte (dwordx4) or 4-byte (dword) load per lane from global `src`
+// into LDS at the wave-uniform address `dst` + 16 (or 4) x lane.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const LDS_AS char*)p);
+}
+__device__ __forceinline__ void lds_dma16(const void* src, const char* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* src, const char* dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
+}
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// Workgroup barrier without a fence: each wave has already waited for its
+// own ring loads (a fence would wait for every outstanding load, including
+// the blocks still streaming in).
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <typename T>
 __device__ __forceinline__ u32x4 ld16(const T* p) {
@@ -286,20 +317,31 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float sl2, float& 
 }
 
 // ----------------------------------------------------------------------------
-// Query tile: up to 128 rows (tokens x group heads) of one request and kv head,
-// keys [kv_begin, kv_end) in 64-key blocks. K/V blocks go straight from HBM/L2
-// to LDS (16-byte direct loads) into two alternating buffers: the next block
-// streams in while the current one is computed, with one barrier per block.
-template <typename T>
+// Query tile: up to 256 rows (tokens x group heads) of one request and kv head,
+// keys [kv_begin, kv_end) in 64-key blocks; wave w owns rows 32w + [0, 32).
+// K/V blocks go straight from HBM/L2 to LDS (16-byte direct loads) through a
+// ring of 4 slots, three blocks ahead of the one computed, with one barrier per
+// block; the eight waves share every block (two per SIMD, so one wave's
+// exponentials run beside the other's MFMAs).
+template <bool kPow2>
+struct PageMap {
+  int shift, mask, size;
+  __device__ __forceinline__ int page(int key) const { return kPow2 ? key >> shift : key / size; }
+  __device__ __forceinline__ int slot(int key) const { return kPow2 ? key & mask : key % size; }
+};
+
+template <typename T, bool kPow2>
 __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg, int kvh, int tok0,
-                          int ntok, int kv_begin, int kv_end, char* bufA, char* bufB) {
+                          int ntok, int kv_begin, int kv_end, char* ring, char* idring) {
   using V8 = typename Dt<T>::v8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
   const int g = p.group_size;
   const int rows = ntok * g;
   const int row = wave * 32 + r32;
   const bool row_ok = row < rows;
+  const bool active = wave * 32 < rows;   // wave-uniform: the wave has rows
   const int tok = tok0 + (row_ok ? row / g : 0);
   const int head = kvh * g + (row_ok ? row % g : 0);
 
@@ -311,34 +353,50 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
   const RowMask rm = row_mask(key_lo, key_hi);
 
-  // Direct loads: wave w issues groups 4w+u (u = 0..3) of both K and V; group i
-  // holds rows i + 16 (lane/16), lane & 15 is the 16-byte slot. K row R sits at
+  // Direct loads: wave w fills groups 2w+u (u = 0, 1) of K and of V; group i
+  // holds rows i + 16 (lane / 16), lane & 15 is the 16-byte slot. K row R sits at
   // (R % 16) * 1024 + (R / 16) * 256 with XOR-swizzled chunks; V row R at
   // (R % 16) * 1088 + (R / 16) * 256 (1088-byte groups: the 4 consecutive rows of
-  // a transpose read land 16 banks apart).
+  // a transpose read land 16 banks apart). Rows past kv_end repeat row
+  // kv_end - 1 (finite values the mask sends to -inf), and blocks past the end
+  // load that row too, so every block issues the same loads.
   const int lq = lane >> 4, lslot = lane & 15;
-  int rr[4], kchunk[4];
+  const PageMap<kPow2> pm{p.page_shift, p.page_size - 1, p.page_size};
+  const int kv_last = kv_end - 1;
+  const char* kbase[2];
+  int rr[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    rr[u] = 4 * wave + u + 16 * lq;
-    kchunk[u] = (lslot ^ swz(rr[u])) << 4;
+  for (int u = 0; u < 2; ++u) {
+    rr[u] = 2 * wave + u + 16 * lq;
+    kbase[u] = r.k + ((lslot ^ swz(rr[u])) << 4);
   }
-  uint32_t pg[4];
-  // Rows past kv_end repeat row kv_end - 1: finite values whose scores the
-  // mask sends to -inf, so they add exactly zero to O.
-  auto load_pages = [&](int kb) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) pg[u] = page_of(r, p, rg.page_start, min(kb + rr[u], kv_end - 1));
+  const char* vbase = r.v + (lslot << 4);
+  // Page ids stream through a per-wave LDS ring too (lane l holds the page of
+  // key kb + l); without a page table the loads read word 0 of the request
+  // table and the identity page is used instead.
+  const bool has_ip = r.indices != nullptr;
+  const int32_t* ip = has_ip ? r.indices + rg.page_start : p.reqs;
+  auto idslot = [&](int blk) { return idring + (blk & (kRingSlots - 1)) * kIdSlot + wave * 256; };
+  auto slot = [&](int blk) { return ring + (blk & (kRingSlots - 1)) * kTileBuf; };
+  auto load_ids = [&](int blk) {
+    const uint32_t pl = (uint32_t)pm.page(min(kv_begin + blk * kTileKeys + lane, kv_last));
+    lds_dma4(ip + (has_ip ? pl : 0u), idslot(blk));
   };
-  auto dma_block = [&](int kb, char* buf) {
+  int32_t pid[2];
+  auto read_ids = [&](int blk) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint64_t ro = row_off(r, p, pg[u], min(kb + rr[u], kv_end - 1));
-      __builtin_amdgcn_global_load_lds((const void*)(r.k + ro + kchunk[u]),
-                                       (LDS_AS void*)(buf + (4 * wave + u) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(r.v + ro + (lslot << 4)),
-                                       (LDS_AS void*)(buf + kTileKBytes + (4 * wave + u) * kTileVGroup),
-                                       16, 0, 0);
+    for (int u = 0; u < 2; ++u) pid[u] = *reinterpret_cast<const int32_t*>(idslot(blk) + rr[u] * 4);
+  };
+  auto dma_block = [&](int blk) {
+    const int kb = kv_begin + blk * kTileKeys;
+    char* dst = slot(blk);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int key = min(kb + rr[u], kv_last);
+      const uint32_t page = has_ip ? (uint32_t)pid[u] : (uint32_t)(rg.page_start + pm.page(key));
+      const uint64_t ro = (uint64_t)page * r.kv_sp_b + (uint32_t)pm.slot(key) * r.kv_st_b;
+      lds_dma16(kbase[u] + ro, dst + (2 * wave + u) * 1024);
+      lds_dma16(vbase + ro, dst + kTileKBytes + (2 * wave + u) * kTileVGroup);
     }
   };
 
@@ -348,7 +406,7 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
 #pragma unroll
   for (int c = 0; c < 8; ++c)
     koff[c] = (krow & 15) * 1024 + (krow >> 4) * kRowBytes + (((hi * 8 + c) ^ swz(krow)) << 4);
-  // V^T operand: lane rows 8(g/2) + i/4 (+4 ld), dims 16(g%2) + 4(i%4)
+  // V^T operand: lane rows 8(g/2) + i/4, dims 16(g%2) + 4(i%4)
   const int vg = lane >> 4, vi = lane & 15;
   const int vlane = kTileKBytes + (8 * (vg >> 1) + (vi >> 2)) * kTileVGroup +
                     (16 * (vg & 1) + 4 * (vi & 3)) * 2;
@@ -359,49 +417,33 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   float m = kNegInf, l = 0.f;
   const float sl2 = r.scale_log2;
 
-  // One 64-key block: S for both 32-key halves (K fragments read ahead of the
-  // MFMAs), one running-max decision, then P0 / PV0 / P1 / PV1 as one
-  // straight-line region so the exp work of one half overlaps the other
-  // half's MFMAs.
-  auto compute_block = [&](int kb, const char* buf) {
-    f32x16 s[2];
-    u32x4 kf[2][8];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) kf[h][c] = lds_ld16(buf, 2 * h * kRowBytes + koff[c]);
+  // Each block b is two phases of a wave:
+  //   M: the score MFMAs of block b (S_b, 16, K from LDS slot b) and the P.V
+  //      MFMAs of block b-1 (16, V^T from slot b-1, P_{b-1} in registers);
+  //   V: mask, running max and exponentials of S_b (P_b and l), VALU only.
+  // Waves 0-3 run M while waves 4-7 (the other wave of each SIMD) run V, then
+  // the other way round, with a barrier between the turns: the MFMA pipe takes
+  // one wave's 32 MFMAs while the VALU runs the other wave's softmax.
+  f32x16 s[2];
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+  V8 pb[2][2];
+  auto m_s = [&](int b) {
+    const char* kb_buf = slot(b);
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 kf = lds_ld16(kb_buf, 2 * h * kRowBytes + koff[c]);
+        s[h] = Dt<T>::mfma(__builtin_bit_cast(V8, kf), qreg[c], s[h]);
+      }
+  };
+  auto m_pv = [&](int b) {
+    const char* vb = slot(b) + vlane;
+#pragma unroll
     for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        s[h] = Dt<T>::mfma(__builtin_bit_cast(V8, kf[h][c]), qreg[c], s[h]);
-    // keep 4 fragment reads in flight ahead of the MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
-
-    if (__any((unsigned)(kb - rm.lo) > rm.span || (unsigned)(kb + kTileKeys - 1 - rm.lo) > rm.span)) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int kidx = kb + h * 32 + acc_key(j, hi);
-          s[h][j] = ((unsigned)(kidx - rm.lo) <= rm.span) ? s[h][j] : kNegInf;
-        }
-    }
-    update_max<2>(s, sl2, m, l, o);
-    const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
-    const char* vb = buf + vlane;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      V8 pb[2];
-      exp_block<T>(s[h], sl2, mu2, l, pb);
 #pragma unroll
       for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
@@ -415,38 +457,113 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
             part[ld] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)pp));
           }
           const u32x4 w = {part[0][0], part[0][1], part[1][0], part[1][1]};
-          o[db] = Dt<T>::mfma(__builtin_bit_cast(V8, w), pb[mp], o[db]);
+          o[db] = Dt<T>::mfma(__builtin_bit_cast(V8, w), pb[h][mp], o[db]);
         }
+  };
+  // M with both parts: score and P.V MFMAs alternate, LDS reads ahead of them.
+  auto m_both = [&](int b) {
+    m_s(b);
+    m_pv(b - 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     }
   };
+  auto v_phase = [&](int b) {
+    __builtin_amdgcn_s_setprio(1);
+    const int kb = kv_begin + b * kTileKeys;
+    if (__any((unsigned)(kb - rm.lo) > rm.span || (unsigned)(kb + kTileKeys - 1 - rm.lo) > rm.span)) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int kidx = kb + h * 32 + acc_key(j, hi);
+          s[h][j] = ((unsigned)(kidx - rm.lo) <= rm.span) ? s[h][j] : kNegInf;
+        }
+    }
+    update_max<2>(s, sl2, m, l, o);
+    const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) exp_block<T>(s[h], sl2, mu2, l, pb[h]);
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-  if (kv_begin < kv_end) {
-    load_pages(kv_begin);
-    dma_block(kv_begin, bufA);
-    if (kv_begin + kTileKeys < kv_end) load_pages(kv_begin + kTileKeys);
+  // Block b streams into ring slot b % 4 and its page ids into id slot b % 4.
+  // Iteration t reads slots t-1 and t and issues the K/V loads of block t+2
+  // (4 loads, into the slot of block t-2) and then the ids
+  // of block t+6 (1 load), and moves the ids of block t+3 to registers. The
+  // prologue issues what iterations -2 and -1 would have.
+  const int nblk = kv_begin < kv_end ? (kv_end - kv_begin + kTileKeys - 1) / kTileKeys : 0;
+  const bool second = wave >= kWaves / 2;   // wave-uniform: the V-first half
+  if (nblk > 0) {
+    load_ids(0);
+    load_ids(1);
+    load_ids(2);
+    load_ids(3);
+    wait_vm<3>();
+    read_ids(0);
+    dma_block(0);
+    load_ids(4);
+    wait_vm<7>();
+    read_ids(1);
+    dma_block(1);
+    load_ids(5);
+    wait_vm<11>();
+    read_ids(2);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kb = kv_begin; kb < kv_end; kb += 2 * kTileKeys) {
-    // block kb in bufA
-    if (kb + kTileKeys < kv_end) {
-      dma_block(kb + kTileKeys, bufB);
-      if (kb + 2 * kTileKeys < kv_end) load_pages(kb + 2 * kTileKeys);
+  // iteration t: wait for block t, then issue block t+2's loads
+  auto top = [&](int t) {
+    // block t landed (and the ids of block t+3, issued before it); the 6 loads
+    // issued after it may still be in flight
+    wait_vm<6>();
+    ring_barrier();
+    dma_block(t + 2);
+    load_ids(t + 6);
+    read_ids(t + 3);
+  };
+  // Iteration t: waves 0-3 run M(t) then V(t), waves 4-7 V(t-1) then M(t),
+  // where M(t) = S_t (t < nblk) and P.V of block t-1 (t > 0). Each half runs
+  // its own straight-line loop; both pass the same 2 (nblk + 1) barriers.
+  if (nblk > 0) {
+    if (!active) {
+      for (int t = 0; t <= nblk; ++t) {
+        top(t);
+        ring_barrier();
+      }
+    } else if (!second) {
+      top(0);
+      m_s(0);
+      ring_barrier();
+      v_phase(0);
+      for (int t = 1; t < nblk; ++t) {
+        top(t);
+        m_both(t);
+        ring_barrier();
+        v_phase(t);
+      }
+      top(nblk);
+      m_pv(nblk - 1);
+      ring_barrier();
+    } else {
+      top(0);
+      ring_barrier();
+      m_s(0);
+      for (int t = 1; t < nblk; ++t) {
+        top(t);
+        v_phase(t - 1);
+        ring_barrier();
+        m_both(t);
+      }
+      top(nblk);
+      v_phase(nblk - 1);
+      ring_barrier();
+      m_pv(nblk - 1);
     }
-    compute_block(kb, bufA);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int kb1 = kb + kTileKeys;
-    if (kb1 >= kv_end) break;
-    // block kb1 in bufB
-    if (kb1 + kTileKeys < kv_end) {
-      dma_block(kb1 + kTileKeys, bufA);
-      if (kb1 + 2 * kTileKeys < kv_end) load_pages(kb1 + 2 * kTileKeys);
-    }
-    compute_block(kb1, bufB);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   }
+  // drain the loads of blocks past the end before the LDS is reused
+  wait_vm<0>();
   l = xhalf_sum(l);
 
   if (row_ok) {
@@ -473,7 +590,7 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
 
 // ----------------------------------------------------------------------------
 // Key chunk: all q_len x group rows (<= 32) of one request and kv head over keys
-// [kv_begin, kv_end). Wave w takes 32-key steps w, w+4, ... Each wave load
+// [kv_begin, kv_end). Wave w takes 32-key steps w, w+8, ... Each wave load
 // instruction covers 4 whole 256-byte rows (16 lanes per row); K and V go to
 // the wave's own LDS blocks, from which the K operand and the V^T operand are
 // read. The next step's rows are in flight while the current step computes,
@@ -481,7 +598,7 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
 // Wave states merge in LDS; split chunks merge through the float workspace.
 template <typename T>
 __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg, int kvh,
-                           int kv_begin, int kv_end, int split, int grp, char* bufA, char* bufB) {
+                           int kv_begin, int kv_end, int split, int grp, char* lds) {
   using V8 = typename Dt<T>::v8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
@@ -499,7 +616,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
   const RowMask rm = row_mask(key_lo, key_hi);
 
-  char* Kw = (wave < 2 ? bufA : bufB) + (wave & 1) * kWaveLds;
+  char* Kw = lds + wave * kWaveLds;
   char* Vw = Kw + kWaveKBytes;
   f32x16 o[4];
 #pragma unroll
@@ -516,18 +633,18 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   // loads: instruction i moves row 4 i + (lane >> 4) of the step, slot lane & 15
   const int ld_row = lane >> 4, ld_slot = lane & 15;
   const int first = kv_begin + kStepKeys * wave;
-  const int n_steps = first < kv_end ? (kv_end - first + 4 * kStepKeys - 1) / (4 * kStepKeys) : 0;
+  const int n_steps = first < kv_end ? (kv_end - first + kWaves * kStepKeys - 1) / (kWaves * kStepKeys) : 0;
   uint32_t pidx[8];
   u32x4 kst[8], vst[8];
   auto load_pages = [&](int i) {
-    const int kb = first + 4 * kStepKeys * i;
+    const int kb = first + kWaves * kStepKeys * i;
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       pidx[c] = page_of(r, p, rg.page_start, min(kb + 4 * c + ld_row, kv_end - 1));
   };
   // rows past kv_end repeat row kv_end - 1 (masked to zero weight)
   auto load_rows = [&](int i) {
-    const int kb = first + 4 * kStepKeys * i;
+    const int kb = first + kWaves * kStepKeys * i;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const uint64_t off = row_off(r, p, pidx[c], min(kb + 4 * c + ld_row, kv_end - 1));
@@ -542,7 +659,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
     if (n_steps > 1) load_pages(1);
   }
   for (int i = 0; i < n_steps; ++i) {
-    const int kb = first + 4 * kStepKeys * i;
+    const int kb = first + kWaves * kStepKeys * i;
     // this step's rows to the wave's blocks; the previous step's reads of them
     // are ordered before these writes (LDS runs a wave's requests in order)
 #pragma unroll
@@ -576,29 +693,31 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   }
   l = xhalf_sum(l);
 
-  // ---- merge the 4 wave states in LDS
+  // ---- merge the wave states in LDS
   __syncthreads();
-  float* sm_m = reinterpret_cast<float*>(bufA);   // [4][32]
-  float* sm_l = sm_m + 128;                       // [4][32]
-  float* accA = sm_l + 128;                       // [128 d][32 rows]
-  float* accB = accA + kHeadDim * 32;
-  int* sm_flag = reinterpret_cast<int*>(accB + kHeadDim * 32);
+  float* sm_m = reinterpret_cast<float*>(lds);    // [waves][32]
+  float* sm_l = sm_m + kWaves * 32;               // [waves][32]
+  float* accs = sm_l + kWaves * 32;               // 4 x [128 d][32 rows]
+  int* sm_flag = reinterpret_cast<int*>(accs + 4 * kHeadDim * 32);
   // wave maxima in scaled (base-2) units
   const float m2 = (m == kNegInf) ? kNegInf : m * sl2;
   if (hi == 0) sm_m[wave * 32 + r32] = m2;
   __syncthreads();
-  const float M = fmaxf(fmaxf(sm_m[r32], sm_m[32 + r32]), fmaxf(sm_m[64 + r32], sm_m[96 + r32]));
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 32 + r32]);
   const float sc = (M == kNegInf) ? 0.f : fast_exp2(m2 - M);
   if (hi == 0) sm_l[wave * 32 + r32] = l * sc;
-  float* acc = (wave & 1) ? accB : accA;
-  if (wave < 2) {
+  // waves w and w + 4 sum into partial sum w % 4
+  float* acc = accs + (wave & 3) * kHeadDim * 32;
+  if (wave < 4) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int j = 0; j < 16; ++j) acc[(db * 32 + acc_d(j, hi)) * 32 + r32] = o[db][j] * sc;
   }
   __syncthreads();
-  if (wave >= 2) {
+  if (wave >= 4) {
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -606,8 +725,9 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   }
   __syncthreads();
 
-  const int frow = threadIdx.x >> 3, d0 = (threadIdx.x & 7) * 16;
-  const bool fok = frow < rows;
+  // final stage on the first 256 threads: row threadIdx / 8, 16 dims each
+  const int frow = (threadIdx.x >> 3) & 31, d0 = (threadIdx.x & 7) * 16;
+  const bool fok = threadIdx.x < 256 && frow < rows;
   const int ftok = fok ? frow / g : 0;
   const int fhead = kvh * g + (fok ? frow % g : 0);
   const int64_t out_row = (int64_t)(rg.qo_start + ftok);
@@ -616,12 +736,19 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   const float sink_l2 = p.sinks ? p.sinks[fhead] * kLog2e : 0.f;
 
   if (fok) {
-    const float Mr = fmaxf(fmaxf(sm_m[frow], sm_m[32 + frow]), fmaxf(sm_m[64 + frow], sm_m[96 + frow]));
-    const float L = sm_l[frow] + sm_l[32 + frow] + sm_l[64 + frow] + sm_l[96 + frow];
+    float Mr = kNegInf, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      Mr = fmaxf(Mr, sm_m[w * 32 + frow]);
+      L += sm_l[w * 32 + frow];
+    }
     const float lse_r = L > 0.f ? Mr + fast_log2(L) : kNegInf;
     float vals[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) vals[i] = accA[(d0 + i) * 32 + frow] + accB[(d0 + i) * 32 + frow];
+    for (int i = 0; i < 16; ++i) {
+      const int e = (d0 + i) * 32 + frow;
+      vals[i] = (accs[e] + accs[kHeadDim * 32 + e]) + (accs[2 * kHeadDim * 32 + e] + accs[3 * kHeadDim * 32 + e]);
+    }
     if (grp < 0) {
       const float mu = (Mr == kNegInf) ? 0.f : Mr;
       float den = L;
@@ -704,9 +831,11 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads, 2) void pod_grid_kernel(Params p) {
-  __shared__ __attribute__((aligned(16))) char bufA[kLdsHalf];
-  __shared__ __attribute__((aligned(16))) char bufB[kLdsHalf];
+__global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params p) {
+  // the query tile's ring slots, or one 18 KB part per key-chunk wave
+  __shared__ __attribute__((aligned(16))) char lds[kLdsMain];
+  // page-id ring of the query tile: 4 slots x 8 waves x 64 words
+  __shared__ __attribute__((aligned(16))) char ids[kRingSlots * kIdSlot];
   const int32_t* it = p.items + (int64_t)blockIdx.x * kItemWords;
   const int flags = it[0];
   if (flags < 0) return;
@@ -717,9 +846,11 @@ __global__ __launch_bounds__(kThreads, 2) void pod_grid_kernel(Params p) {
   const int32_t* rq = p.reqs + req * kReqWords;
   RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
   if (flags & kFlagChunk)
-    chunk_item<T>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, bufA, bufB);
+    chunk_item<T>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds);
+  else if (p.page_shift >= 0)
+    tile_item<T, true>(p, r, rg, kvh, tok0, ntok, kv_begin, kv_end, lds, ids);
   else
-    tile_item<T>(p, r, rg, kvh, tok0, ntok, kv_begin, kv_end, bufA, bufB);
+    tile_item<T, false>(p, r, rg, kvh, tok0, ntok, kv_begin, kv_end, lds, ids);
 }
 
 }  // namespace

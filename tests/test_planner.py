@@ -48,7 +48,7 @@ def check_coverage(img, roles, hqo, hkv):
             if grp >= 0:
                 group_members.setdefault(grp, []).append(flags >> 8)
         else:
-            assert ntok * g <= 128 and grp == -1
+            assert ntok * g <= 256 and grp == -1
             rows = range(tok0, tok0 + ntok)
         assert 0 <= kb < ke <= kv_len
         for i in rows:
