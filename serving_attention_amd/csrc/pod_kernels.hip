@@ -491,8 +491,8 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   };
 
   // Block b streams into ring slot b % 4 and its page ids into id slot b % 4.
-  // Iteration t reads slots t-1 and t and issues the K/V loads of block t+2
-  // (4 loads, into the slot of block t-2) and then the ids
+  // Iteration t reads slots t-1 and t and, between its two turns, issues the
+  // K/V loads of block t+2 (4 loads, into the slot of block t-2) and then the ids
   // of block t+6 (1 load), and moves the ids of block t+3 to registers. The
   // prologue issues what iterations -2 and -1 would have.
   const int nblk = kv_begin < kv_end ? (kv_end - kv_begin + kTileKeys - 1) / kTileKeys : 0;
@@ -519,6 +519,11 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
     // issued after it may still be in flight
     wait_vm<6>();
     ring_barrier();
+  };
+  // the barrier between the turns, then block t+2's loads (issued here, not
+  // at the top, the two turns take equally long)
+  auto mid = [&](int t) {
+    ring_barrier();
     dma_block(t + 2);
     load_ids(t + 6);
     read_ids(t + 3);
@@ -530,35 +535,35 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
     if (!active) {
       for (int t = 0; t <= nblk; ++t) {
         top(t);
-        ring_barrier();
+        mid(t);
       }
     } else if (!second) {
       top(0);
       m_s(0);
-      ring_barrier();
+      mid(0);
       v_phase(0);
       for (int t = 1; t < nblk; ++t) {
         top(t);
         m_both(t);
-        ring_barrier();
+        mid(t);
         v_phase(t);
       }
       top(nblk);
       m_pv(nblk - 1);
-      ring_barrier();
+      mid(nblk);
     } else {
       top(0);
-      ring_barrier();
+      mid(0);
       m_s(0);
       for (int t = 1; t < nblk; ++t) {
         top(t);
         v_phase(t - 1);
-        ring_barrier();
+        mid(t);
         m_both(t);
       }
       top(nblk);
       v_phase(nblk - 1);
-      ring_barrier();
+      mid(nblk);
       m_pv(nblk - 1);
     }
   }
