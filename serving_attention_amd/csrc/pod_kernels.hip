@@ -387,17 +387,19 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
 #pragma unroll
     for (int u = 0; u < 2; ++u) pid[u] = *reinterpret_cast<const int32_t*>(idslot(blk) + rr[u] * 4);
   };
-  auto dma_block = [&](int blk) {
+  // the K and V loads of the wave's row group u of block blk
+  auto dma_rows = [&](int blk, int u) {
     const int kb = kv_begin + blk * kTileKeys;
     char* dst = slot(blk);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = min(kb + rr[u], kv_last);
-      const uint32_t page = has_ip ? (uint32_t)pid[u] : (uint32_t)(rg.page_start + pm.page(key));
-      const uint64_t ro = (uint64_t)page * r.kv_sp_b + (uint32_t)pm.slot(key) * r.kv_st_b;
-      lds_dma16(kbase[u] + ro, dst + (2 * wave + u) * 1024);
-      lds_dma16(vbase + ro, dst + kTileKBytes + (2 * wave + u) * kTileVGroup);
-    }
+    const int key = min(kb + rr[u], kv_last);
+    const uint32_t page = has_ip ? (uint32_t)pid[u] : (uint32_t)(rg.page_start + pm.page(key));
+    const uint64_t ro = (uint64_t)page * r.kv_sp_b + (uint32_t)pm.slot(key) * r.kv_st_b;
+    lds_dma16(kbase[u] + ro, dst + (2 * wave + u) * 1024);
+    lds_dma16(vbase + ro, dst + kTileKBytes + (2 * wave + u) * kTileVGroup);
+  };
+  auto dma_block = [&](int blk) {
+    dma_rows(blk, 0);
+    dma_rows(blk, 1);
   };
 
   // K operand: lane reads row h*32 + key_row(r32), chunk hi*8 + c
@@ -520,11 +522,10 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
     wait_vm<6>();
     ring_barrier();
   };
-  // the barrier between the turns, then block t+2's loads (issued here, not
-  // at the top, the two turns take equally long)
-  auto mid = [&](int t) {
-    ring_barrier();
-    dma_block(t + 2);
+  // Block t+2's loads go out in two parts, one at the start of each turn of
+  // the wave (all eight waves issuing all their loads at one point queue up
+  // behind each other); then the ids of block t+6.
+  auto ids = [&](int t) {
     load_ids(t + 6);
     read_ids(t + 3);
   };
@@ -535,36 +536,57 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
     if (!active) {
       for (int t = 0; t <= nblk; ++t) {
         top(t);
-        mid(t);
+        dma_rows(t + 2, 0);
+        ring_barrier();
+        dma_rows(t + 2, 1);
+        ids(t);
       }
     } else if (!second) {
       top(0);
+      dma_rows(2, 0);
       m_s(0);
-      mid(0);
+      ring_barrier();
+      dma_rows(2, 1);
+      ids(0);
       v_phase(0);
       for (int t = 1; t < nblk; ++t) {
         top(t);
+        dma_rows(t + 2, 0);
         m_both(t);
-        mid(t);
+        ring_barrier();
+        dma_rows(t + 2, 1);
+        ids(t);
         v_phase(t);
       }
       top(nblk);
+      dma_rows(nblk + 2, 0);
       m_pv(nblk - 1);
-      mid(nblk);
+      ring_barrier();
+      dma_rows(nblk + 2, 1);
+      ids(nblk);
     } else {
       top(0);
-      mid(0);
+      dma_rows(2, 0);
+      ring_barrier();
       m_s(0);
+      dma_rows(2, 1);
+      ids(0);
       for (int t = 1; t < nblk; ++t) {
         top(t);
+        dma_rows(t + 2, 0);
         v_phase(t - 1);
-        mid(t);
+        ring_barrier();
         m_both(t);
+        dma_rows(t + 2, 1);
+        ids(t);
       }
       top(nblk);
+      dma_rows(nblk + 2, 0);
       v_phase(nblk - 1);
-      mid(nblk);
+      ring_barrier();
       m_pv(nblk - 1);
+      dma_rows(nblk + 2, 1);
+      ids(nblk);
     }
   }
   // drain the loads of blocks past the end before the LDS is reused
