@@ -75,12 +75,16 @@ constexpr int kRowBytes = kHeadDim * 2;       // one kv head's K row (16-bit typ
 constexpr int kVRowBytes = kRowBytes + 64;    // V rows are padded by 64 bytes
 constexpr int kTileKeys = 64;                 // keys per LDS block of a query tile
 constexpr int kStepKeys = 32;                 // keys per wave step of a key chunk
-constexpr int kTileKBytes = kTileKeys * kRowBytes;                         // 16 KB
-// Query-tile V block: logical row R sits in 1088-byte group R % 16 at slot R / 16,
-// so each group is one lane-contiguous direct-to-LDS load of 4 rows and the 4
-// consecutive rows of a transpose read land 16 banks apart.
+// Query-tile K block: row R sits in 1040-byte group R % 16 at slot R / 16, so
+// each group is one lane-contiguous direct-to-LDS load of 4 rows, the 16
+// rows read at one 16-byte chunk fall in 16 distinct bank groups, and the
+// chunk offset of a fragment read is an instruction constant.
+constexpr int kTileKGroup = 4 * kRowBytes + 16;
+constexpr int kTileKBytes = 16 * kTileKGroup;                               // 16.25 KB
+// Query-tile V block: row R sits in 1088-byte group R % 16 at slot R / 16, so
+// the 4 consecutive rows of a transpose read land 16 banks apart.
 constexpr int kTileVGroup = 4 * kRowBytes + 64;
-constexpr int kTileBuf = kTileKBytes + 16 * kTileVGroup;                    // 33 KB per buffer
+constexpr int kTileBuf = kTileKBytes + 16 * kTileVGroup;                    // 33.25 KB per buffer
 constexpr int kWaveKBytes = kStepKeys * kRowBytes;
 constexpr int kWaveLds = kWaveKBytes + kStepKeys * kVRowBytes;              // 18 KB
 constexpr int kWaves = kThreads / 64;                                      // 8 waves
@@ -361,6 +365,7 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   // kv_end - 1 (finite values the mask sends to -inf), and blocks past the end
   // load that row too, so every block issues the same loads.
   const int lq = lane >> 4, lslot = lane & 15;
+  const int nblk = kv_begin < kv_end ? (kv_end - kv_begin + kTileKeys - 1) / kTileKeys : 0;
   const PageMap<kPow2> pm{p.page_shift, p.page_size - 1, p.page_size};
   const int kv_last = kv_end - 1;
   const char* kbase[2];
@@ -368,7 +373,7 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     rr[u] = 2 * wave + u + 16 * lq;
-    kbase[u] = r.k + ((lslot ^ swz(rr[u])) << 4);
+    kbase[u] = r.k + (lslot << 4);
   }
   const char* vbase = r.v + (lslot << 4);
   // Page ids stream through a per-wave LDS ring too (lane l holds the page of
@@ -394,7 +399,7 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
     const int key = min(kb + rr[u], kv_last);
     const uint32_t page = has_ip ? (uint32_t)pid[u] : (uint32_t)(rg.page_start + pm.page(key));
     const uint64_t ro = (uint64_t)page * r.kv_sp_b + (uint32_t)pm.slot(key) * r.kv_st_b;
-    lds_dma16(kbase[u] + ro, dst + (2 * wave + u) * 1024);
+    lds_dma16(kbase[u] + ro, dst + (2 * wave + u) * kTileKGroup);
     lds_dma16(vbase + ro, dst + kTileKBytes + (2 * wave + u) * kTileVGroup);
   };
   auto dma_block = [&](int blk) {
@@ -402,12 +407,10 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
     dma_rows(blk, 1);
   };
 
-  // K operand: lane reads row h*32 + key_row(r32), chunk hi*8 + c
+  // K operand: lane reads row h*32 + key_row(r32), chunk hi*8 + c, at
+  // klane + h*512 + c*16
   const int krow = key_row(r32);
-  int koff[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c)
-    koff[c] = (krow & 15) * 1024 + (krow >> 4) * kRowBytes + (((hi * 8 + c) ^ swz(krow)) << 4);
+  const int klane = (krow & 15) * kTileKGroup + (krow >> 4) * kRowBytes + hi * 128;
   // V^T operand: lane rows 8(g/2) + i/4, dims 16(g%2) + 4(i%4)
   const int vg = lane >> 4, vi = lane & 15;
   const int vlane = kTileKBytes + (8 * (vg >> 1) + (vi >> 2)) * kTileVGroup +
@@ -438,7 +441,7 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
     for (int c = 0; c < 8; ++c)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const u32x4 kf = lds_ld16(kb_buf, 2 * h * kRowBytes + koff[c]);
+        const u32x4 kf = lds_ld16(kb_buf + klane, 2 * h * kRowBytes + c * 16);
         s[h] = Dt<T>::mfma(__builtin_bit_cast(V8, kf), qreg[c], s[h]);
       }
   };
@@ -497,7 +500,6 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   // K/V loads of block t+2 (4 loads, into the slot of block t-2) and then the ids
   // of block t+6 (1 load), and moves the ids of block t+3 to registers. The
   // prologue issues what iterations -2 and -1 would have.
-  const int nblk = kv_begin < kv_end ? (kv_end - kv_begin + kTileKeys - 1) / kTileKeys : 0;
   const bool second = wave >= kWaves / 2;   // wave-uniform: the V-first half
   if (nblk > 0) {
     load_ids(0);
