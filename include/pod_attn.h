@@ -166,7 +166,7 @@ typedef struct pod_plan_info {
   int32_t n_decode_items;
   int32_t n_groups;         /* split (request, kv head) units that need the LSE merge */
   int32_t n_slots;          /* partial-state slots in the float workspace */
-  int32_t grid;             /* workgroups launched (>= n_items; holes are idle) */
+  int32_t grid;             /* persistent workgroups launched (one per CU) */
   int32_t decode_chunk;     /* keys per decode split actually used */
   int32_t image_ints;       /* int32 words of the work-list image */
   int64_t float_ws_bytes;   /* float workspace the plan needs */
@@ -227,18 +227,30 @@ int pod_plan_compute(const pod_plan_desc* desc, int32_t* image, size_t image_cap
  * Work-list image layout (int32 words), for inspection by tools and tests.
  *   header[POD_HDR_WORDS]: [0] magic POD_IMAGE_MAGIC, [1] n_items, [2] grid,
  *     [3] n_reqs, [4] n_groups, [5] reqs_off, [6] items_off, [7] groups_off,
- *     [8] counters_off, [9] n_slots, [10] slot_floats, [11] decode_chunk.
+ *     [8] counters_off, [9] n_slots, [10] slot_floats, [11] decode_chunk,
+ *     [12] wgs_off, [13] blocks_off, [14] n_blocks, [15] pool_first,
+ *     [16] pool_count, [17] queue_off.
  *   reqs[n_reqs][4]: {qo_start, qo_len, kv_len, page_start} per request, prefill
  *     requests first, then decode requests.
- *   items[grid][8]: {flags, req, kv_head, tok0, ntok, kv_begin, kv_end, group}; slot b
- *     is the item of workgroup b. flags bit 0: role (0 prefill, 1 decode); bit 1:
- *     kind (0 = query tile of up to 128 rows, 1 = key chunk of all q_len*group
- *     rows, <= 32); bits 8..: split index; flags == -1 marks an idle slot.
- *     group == -1: the item writes its output directly.
+ *   items[n_items][8]: {flags, req, kv_head, tok0, ntok, kv_begin, kv_end, group}.
+ *     flags bit 0: role (0 prefill, 1 decode); bit 1: kind (0 = query tile of up
+ *     to 256 rows, 1 = key chunk of all q_len*group rows, <= 32); bits 8..: split
+ *     index. group == -1: the item writes its output directly. Items are grouped
+ *     by workgroup (its query tiles, then its key chunks); the last pool_count
+ *     items, from pool_first on, are key chunks that any workgroup takes from a
+ *     shared queue once its own list is done.
+ *   wgs[grid][8]: per persistent workgroup {first item, query tiles, key chunks,
+ *     first block, blocks, chunks run first (0/1), prefill-role tiles, blocks of
+ *     those}. Workgroup w runs on die w % 8.
+ *   blocks[n_blocks][4]: the query tiles' 64-key blocks in each workgroup's order:
+ *     {first key, last key of the item, first page of the request, meta}; meta
+ *     bit 31 first block of its item, bit 30 role, bits 16..29 kv head, bits
+ *     0..15 tile index in the workgroup's list.
  *   groups[n_groups][4]: {n_splits, first_slot, req, kv_head}.
  *   counters[n_groups]: arrival counters, zero in the image.
+ *   queue[2]: next pool item and workgroups done with the pool, zero in the image.
  */
-enum { POD_HDR_WORDS = 16, POD_IMAGE_MAGIC = 0x504f4431 };
+enum { POD_HDR_WORDS = 24, POD_IMAGE_MAGIC = 0x504f4431 };
 
 #ifdef __cplusplus
 }

@@ -26,7 +26,7 @@ POD_ORDER_PREFILL_FIRST = 1
 POD_ORDER_DECODE_FIRST = 2
 POD_ORDER_LONGEST_FIRST = 3
 
-POD_HDR_WORDS = 16
+POD_HDR_WORDS = 24
 POD_IMAGE_MAGIC = 0x504F4431
 
 EXPORTED = (

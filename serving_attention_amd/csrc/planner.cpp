@@ -39,17 +39,19 @@ int fail(std::string* err, int code, const std::string& msg) {
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Relative cost estimates used only to order and place items, in integer
-// units of roughly a nanosecond of one workgroup slot: a query tile costs
-// ~40 ns per key (128 rows x 64-key blocks at ~2.5 us per block), a key chunk
-// ~26 ns per key (512 bytes per key, with the HBM shared by the chunks that
-// run beside the tiles). Measured per item on MI355X.
-constexpr int64_t kTileCostPerKey = 40;
-constexpr int64_t kChunkCostPerKey = 26;
-// POD_ORDER_INTERLEAVE places decode items ahead of their cost share by this
-// factor, so the decode work (whose items are all of similar size) is done
-// at ~80% of each die's list and the lightest query tiles fill the tail.
-constexpr double kDecodeLead = 1.25;
+// Cost estimates used only to place and order items, in nanoseconds of one
+// persistent workgroup (one CU) on MI355X: a query tile streams 64-key blocks at
+// ~2.1 us each (~33 ns per key) plus ~1.5 us at its boundary (output store and
+// the next tile's query load); a key chunk moves 512 bytes per key at ~20 ns per
+// key plus ~2.5 us to start its load pipeline. Measured per item.
+constexpr int64_t kTileCostPerKey = 33;
+constexpr int64_t kTileCostFixed = 1500;
+constexpr int64_t kChunkCostPerKey = 20;
+constexpr int64_t kChunkCostFixed = 2500;
+// Share of the key chunks' estimated cost left to a shared queue that the
+// workgroups drain once their own lists are done: it absorbs what the estimates
+// miss (dies and CUs do not all stream HBM at the same rate).
+constexpr double kPoolShare = 0.25;
 
 int validate_role(const pod_role_desc& r, const char* name, int page_size, std::string* err) {
   char buf[256];
@@ -117,11 +119,14 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   if (d.order < 0 || d.order > 3) return fail(err, POD_ERR_INVALID, "unknown order policy");
   const int g = d.num_qo_heads / d.num_kv_heads;
   if (g > kMaxGroup) return fail(err, POD_ERR_UNSUPPORTED, "group size above 128 is not supported");
+  if (d.num_kv_heads > kMaxKvHeads) return fail(err, POD_ERR_UNSUPPORTED, "more than 16384 kv heads");
+  if (d.has_sinks && d.num_qo_heads > kMaxSinkHeads)
+    return fail(err, POD_ERR_UNSUPPORTED, "sinks with more than 1024 qo heads are not supported");
   int rc = validate_role(d.prefill, "prefill", d.page_size, err);
   if (rc) return rc;
   rc = validate_role(d.decode, "decode", d.page_size, err);
   if (rc) return rc;
-  const int num_cus = d.num_cus > 0 ? d.num_cus : 256;
+  const int num_cus = d.num_cus > 0 ? d.num_cus : 256;   // >= 1
   const int H = d.num_kv_heads;
 
   // per-request table: prefill requests first, then decode requests
@@ -203,7 +208,7 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
           it.w[5] = (int32_t)b0;
           it.w[6] = (int32_t)b1;
           it.w[7] = grp;
-          it.cost = kChunkCostPerKey * (b1 - b0);
+          it.cost = kChunkCostFixed + kChunkCostPerKey * (b1 - b0);
           it.xcd = -1;
         }
       }
@@ -223,7 +228,7 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
           it.w[5] = (int32_t)lo;
           it.w[6] = (int32_t)hi;
           it.w[7] = -1;
-          it.cost = kTileCostPerKey * (hi - lo);
+          it.cost = kTileCostFixed + kTileCostPerKey * (hi - lo);
           // tiles sharing one request's K/V for one kv head stay on one die (L2 reuse)
           it.xcd = (int32_t)((ri * (size_t)H + kvh) % kNumXcds);
         }
@@ -232,8 +237,12 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   }
 
   // Heaviest first: a stable counting sort on the cost quantised to 1024 levels.
-  int64_t max_cost = 1;
-  for (const Item& it : items) max_cost = std::max(max_cost, it.cost);
+  int64_t max_cost = 1, total_cost = 0, max_tile_cost = 0;
+  for (const Item& it : items) {
+    max_cost = std::max(max_cost, it.cost);
+    total_cost += it.cost;
+    if (!(it.w[0] & kFlagChunk)) max_tile_cost = std::max(max_tile_cost, it.cost);
+  }
   constexpr int kLevels = 1024;
   std::vector<int32_t> bucket_start(kLevels + 1, 0);
   std::vector<int16_t> level(items.size());
@@ -248,64 +257,120 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   std::vector<uint32_t> order(items.size());
   for (size_t i = 0; i < items.size(); ++i) order[bucket_start[level[i]]++] = (uint32_t)i;
 
-  // Place items on dies. Tiles keep their die; key chunks go to the least
-  // loaded die, heaviest first (LPT).
+  // Dies. The query tiles of one (request, kv head) unit share its K/V, so a
+  // unit gets a home die (units heaviest first onto the least loaded die) and
+  // its tiles go there unless that die would pass an even share of all work by
+  // more than one tile (few large units then still spread over every die).
+  // Key chunks then fill the least loaded dies, heaviest first.
   int64_t load[kNumXcds] = {};
-  for (const Item& it : items)
-    if (it.xcd >= 0) load[it.xcd] += it.cost;
-  for (uint32_t i : order) {
-    Item& it = items[i];
-    if (it.xcd >= 0) continue;
-    int best = 0;
-    for (int x = 1; x < kNumXcds; ++x)
-      if (load[x] < load[best]) best = x;
-    it.xcd = best;
-    load[best] += it.cost;
-  }
-
-  // Per die: each role's items heaviest first; POD_ORDER_INTERLEAVE merges the
-  // two roles in proportion to their cost so both kinds are resident on every
-  // CU at once (the HBM-bound decode items then never all run together), and
-  // POD_ORDER_LONGEST_FIRST merges them heaviest first.
-  std::vector<uint32_t> per_pre[kNumXcds], per_dec[kNumXcds];
-  int64_t tp[kNumXcds] = {}, td[kNumXcds] = {};
   {
-    size_t np[kNumXcds] = {}, nd[kNumXcds] = {};
-    for (const Item& it : items) ++((it.w[0] & kFlagRole) ? nd : np)[it.xcd];
-    for (int x = 0; x < kNumXcds; ++x) {
-      per_pre[x].reserve(np[x]);
-      per_dec[x].reserve(nd[x]);
+    std::vector<int64_t> unit_cost(reqs.size() * (size_t)H, 0);
+    for (const Item& it : items)
+      if (!(it.w[0] & kFlagChunk)) unit_cost[(size_t)it.w[1] * H + it.w[2]] += it.cost;
+    std::vector<uint32_t> units;
+    for (size_t u = 0; u < unit_cost.size(); ++u)
+      if (unit_cost[u] > 0) units.push_back((uint32_t)u);
+    std::stable_sort(units.begin(), units.end(),
+                     [&](uint32_t x, uint32_t y) { return unit_cost[x] > unit_cost[y]; });
+    std::vector<int8_t> home(unit_cost.size(), 0);
+    int64_t uload[kNumXcds] = {};
+    for (uint32_t u : units) {
+      int best = 0;
+      for (int x = 1; x < kNumXcds; ++x)
+        if (uload[x] < uload[best]) best = x;
+      home[u] = (int8_t)best;
+      uload[best] += unit_cost[u];
+    }
+    const int64_t cap = (total_cost + kNumXcds - 1) / kNumXcds + max_tile_cost;
+    for (uint32_t i : order) {
+      Item& it = items[i];
+      if (it.w[0] & kFlagChunk) continue;
+      int x = home[(size_t)it.w[1] * H + it.w[2]];
+      if (load[x] + it.cost > cap) {
+        x = 0;
+        for (int y = 1; y < kNumXcds; ++y)
+          if (load[y] < load[x]) x = y;
+      }
+      it.xcd = x;
+      load[x] += it.cost;
+    }
+    for (uint32_t i : order) {
+      Item& it = items[i];
+      if (!(it.w[0] & kFlagChunk)) continue;
+      int x = 0;
+      for (int y = 1; y < kNumXcds; ++y)
+        if (load[y] < load[x]) x = y;
+      it.xcd = x;
+      load[x] += it.cost;
     }
   }
-  for (uint32_t i : order) {
-    const Item& it = items[i];
-    if (it.w[0] & kFlagRole) {
-      per_dec[it.xcd].push_back(i);
-      td[it.xcd] += it.cost;
-    } else {
-      per_pre[it.xcd].push_back(i);
-      tp[it.xcd] += it.cost;
-    }
-  }
-  size_t max_len = 0;
-  for (int x = 0; x < kNumXcds; ++x) max_len = std::max(max_len, per_pre[x].size() + per_dec[x].size());
 
-  const int64_t grid = (int64_t)max_len * kNumXcds;
+  // The shared pool: the lightest key chunks, up to kPoolShare of their cost.
+  const int G = num_cus;
+  std::vector<uint8_t> in_pool(items.size(), 0);
+  std::vector<uint32_t> pool;
+  {
+    int64_t chunk_cost = 0;
+    for (const Item& it : items)
+      if (it.w[0] & kFlagChunk) chunk_cost += it.cost;
+    const int64_t budget = (int64_t)(kPoolShare * (double)chunk_cost);
+    int64_t taken = 0;
+    for (size_t k = order.size(); k-- > 0 && G > 1;) {   // lightest first
+      const Item& it = items[order[k]];
+      if (!(it.w[0] & kFlagChunk)) continue;
+      if (taken + it.cost > budget) break;
+      taken += it.cost;
+      in_pool[order[k]] = 1;
+    }
+    for (uint32_t i : order)   // the queue hands them out heaviest first
+      if (in_pool[i]) pool.push_back(i);
+  }
+
+  // Workgroups: one persistent workgroup per CU; workgroup w is dispatched to
+  // die w % kNumXcds. Each die's items, heaviest first, go to the least loaded
+  // of its workgroups (LPT), so every workgroup holds a static list.
+  std::vector<std::vector<uint32_t>> wg_tiles(G), wg_chunks(G);
+  std::vector<int64_t> wg_load(G, 0);
+  for (uint32_t i : order) {
+    if (in_pool[i]) continue;
+    const Item& it = items[i];
+    int best = -1;
+    for (int w = it.xcd; w < G; w += kNumXcds)
+      if (best < 0 || wg_load[w] < wg_load[best]) best = w;
+    if (best < 0) best = (int)(i % (uint32_t)G);   // fewer workgroups than dies
+    wg_load[best] += it.cost;
+    ((it.w[0] & kFlagChunk) ? wg_chunks : wg_tiles)[best].push_back(i);
+  }
+  // a workgroup's query tiles run as one block stream per role: prefill first
+  for (int w = 0; w < G; ++w)
+    std::stable_partition(wg_tiles[w].begin(), wg_tiles[w].end(),
+                          [&](uint32_t i) { return (items[i].w[0] & kFlagRole) == 0; });
+
+  // query-tile blocks per workgroup
+  int64_t n_blocks = 0;
+  for (int w = 0; w < G; ++w) {
+    if (wg_tiles[w].size() >= (size_t)kMaxTilesPerWg)
+      return fail(err, POD_ERR_UNSUPPORTED, "plan too large (query tiles per workgroup)");
+    for (uint32_t i : wg_tiles[w]) n_blocks += (items[i].w[6] - items[i].w[5] + kTileKeys - 1) / kTileKeys;
+  }
+
   const int n_groups = (int)(groups.size() / kGroupWords);
   const int64_t reqs_off = POD_HDR_WORDS;
   const int64_t items_off = reqs_off + (int64_t)reqs.size() * kReqWords;
-  const int64_t groups_off = items_off + grid * kItemWords;
+  const int64_t wgs_off = items_off + (int64_t)items.size() * kItemWords;
+  const int64_t blocks_off = wgs_off + (int64_t)G * kWgWords;
+  const int64_t groups_off = blocks_off + n_blocks * kBlockWords;
   const int64_t counters_off = groups_off + (int64_t)n_groups * kGroupWords;
-  const int64_t total = counters_off + n_groups;
-  if (grid > INT32_MAX / 2 || total > INT32_MAX / 2)
-    return fail(err, POD_ERR_UNSUPPORTED, "plan too large");
+  const int64_t queue_off = counters_off + n_groups;
+  const int64_t total = queue_off + 2;
+  if (total > INT32_MAX / 2) return fail(err, POD_ERR_UNSUPPORTED, "plan too large");
 
   image.resize((size_t)total);
   int32_t* h = image.data();
   std::fill(h, h + POD_HDR_WORDS, 0);
   h[0] = POD_IMAGE_MAGIC;
   h[1] = (int32_t)items.size();
-  h[2] = (int32_t)grid;
+  h[2] = G;
   h[3] = (int32_t)reqs.size();
   h[4] = n_groups;
   h[5] = (int32_t)reqs_off;
@@ -315,6 +380,12 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   h[9] = n_slots;
   h[10] = kSlotFloats;
   h[11] = (int32_t)std::min<int64_t>(C, INT32_MAX);
+  h[12] = (int32_t)wgs_off;
+  h[13] = (int32_t)blocks_off;
+  h[14] = (int32_t)n_blocks;
+  h[15] = (int32_t)(items.size() - pool.size());
+  h[16] = (int32_t)pool.size();
+  h[17] = (int32_t)queue_off;
   for (size_t i = 0; i < reqs.size(); ++i) {
     int32_t* q = h + reqs_off + i * kReqWords;
     q[0] = reqs[i].qo_start;
@@ -323,42 +394,72 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
     q[3] = reqs[i].page_start;
   }
   int n_pre = 0, n_dec = 0;
-  for (int x = 0; x < kNumXcds; ++x) {
-    const std::vector<uint32_t>& pre = per_pre[x];
-    const std::vector<uint32_t>& dec = per_dec[x];
-    size_t a = 0, b = 0, k = 0;
-    int64_t cp = 0, cd = 0;
-    while (a < pre.size() || b < dec.size()) {
-      bool take_pre;
-      if (a == pre.size()) take_pre = false;
-      else if (b == dec.size()) take_pre = true;
-      else if (d.order == POD_ORDER_PREFILL_FIRST) take_pre = true;
-      else if (d.order == POD_ORDER_DECODE_FIRST) take_pre = false;
-      else if (d.order == POD_ORDER_LONGEST_FIRST) take_pre = items[pre[a]].cost >= items[dec[b]].cost;
-      else   // cp/tp <= kDecodeLead * cd/td: decode runs ahead of its cost share
-        take_pre = (double)cp * (double)td[x] <= kDecodeLead * (double)cd * (double)tp[x];
-      const Item& it = items[take_pre ? pre[a] : dec[b]];
-      if (take_pre) { cp += it.cost; ++a; ++n_pre; }
-      else { cd += it.cost; ++b; ++n_dec; }
-      int32_t* w = h + items_off + ((int64_t)k * kNumXcds + x) * kItemWords;
-      for (int j = 0; j < kItemWords; ++j) w[j] = it.w[j];
-      ++k;
+  int64_t k = 0, blk = 0;
+  for (int w = 0; w < G; ++w) {
+    const std::vector<uint32_t>& tl = wg_tiles[w];
+    const std::vector<uint32_t>& cl = wg_chunks[w];
+    int32_t* wg = h + wgs_off + (int64_t)w * kWgWords;
+    bool chunks_first;
+    if (tl.empty() || cl.empty()) chunks_first = false;
+    else if (d.order == POD_ORDER_PREFILL_FIRST) chunks_first = false;
+    else if (d.order == POD_ORDER_DECODE_FIRST) chunks_first = true;
+    else if (d.order == POD_ORDER_LONGEST_FIRST) chunks_first = items[cl[0]].cost > items[tl[0]].cost;
+    else chunks_first = ((w / kNumXcds) & 1) != 0;   // half of each die's workgroups each way
+    wg[0] = (int32_t)k;
+    wg[1] = (int32_t)tl.size();
+    wg[2] = (int32_t)cl.size();
+    wg[3] = (int32_t)blk;
+    wg[5] = chunks_first ? 1 : 0;
+    int64_t nb = 0;
+    int32_t n_pre_tiles = 0, n_pre_blocks = 0;
+    for (size_t j = 0; j < tl.size(); ++j) {
+      const Item& it = items[tl[j]];
+      if ((it.w[0] & kFlagRole) == 0) {
+        ++n_pre_tiles;
+        n_pre_blocks += (it.w[6] - it.w[5] + kTileKeys - 1) / kTileKeys;
+      }
+      const int32_t lo = it.w[5], hi = it.w[6];
+      const uint32_t meta = ((uint32_t)(it.w[0] & kFlagRole) << kEntRoleShift) |
+                            ((uint32_t)it.w[2] << kEntKvhShift) | (uint32_t)j;
+      for (int32_t kb = lo; kb < hi; kb += kTileKeys, ++nb) {
+        int32_t* e = h + blocks_off + (blk + nb) * kBlockWords;
+        e[0] = kb;
+        e[1] = hi - 1;
+        e[2] = reqs[it.w[1]].page_start;
+        e[3] = (int32_t)(meta | (kb == lo ? kEntFirst : 0u));
+      }
     }
-    for (; k < max_len; ++k) {   // idle slots
-      int32_t* w = h + items_off + ((int64_t)k * kNumXcds + x) * kItemWords;
-      w[0] = -1;
-      for (int j = 1; j < kItemWords; ++j) w[j] = 0;
-    }
+    wg[4] = (int32_t)nb;
+    wg[6] = n_pre_tiles;
+    wg[7] = n_pre_blocks;
+    blk += nb;
+    for (const std::vector<uint32_t>* lst : {&tl, &cl})
+      for (uint32_t i : *lst) {
+        const Item& it = items[i];
+        int32_t* dst = h + items_off + k * kItemWords;
+        for (int j = 0; j < kItemWords; ++j) dst[j] = it.w[j];
+        ++k;
+        ++((it.w[0] & kFlagRole) ? n_dec : n_pre);
+      }
+  }
+  for (uint32_t i : pool) {
+    const Item& it = items[i];
+    int32_t* dst = h + items_off + k * kItemWords;
+    for (int j = 0; j < kItemWords; ++j) dst[j] = it.w[j];
+    ++k;
+    ++((it.w[0] & kFlagRole) ? n_dec : n_pre);
   }
   for (int i = 0; i < n_groups * kGroupWords; ++i) h[groups_off + i] = groups[i];
   for (int i = 0; i < n_groups; ++i) h[counters_off + i] = 0;
+  h[queue_off] = 0;
+  h[queue_off + 1] = 0;
 
   info.n_items = (int32_t)items.size();
   info.n_prefill_items = n_pre;
   info.n_decode_items = n_dec;
   info.n_groups = n_groups;
   info.n_slots = n_slots;
-  info.grid = (int32_t)grid;
+  info.grid = G;
   info.decode_chunk = (int32_t)std::min<int64_t>(C, INT32_MAX);
   info.image_ints = (int32_t)total;
   info.float_ws_bytes = (int64_t)n_slots * kSlotFloats * 4;

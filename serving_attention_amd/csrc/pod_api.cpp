@@ -285,8 +285,13 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
   int32_t* iws = reinterpret_cast<int32_t*>(ctx->int_ws);
   p.reqs = iws + ctx->hdr[5];
   p.items = iws + ctx->hdr[6];
+  p.wgs = iws + ctx->hdr[12];
+  p.blocks = iws + ctx->hdr[13];
   p.groups = iws + ctx->hdr[7];
   p.counters = iws + ctx->hdr[8];
+  p.queue = iws + ctx->hdr[17];
+  p.pool_first = ctx->hdr[15];
+  p.pool_count = ctx->hdr[16];
   p.partials = reinterpret_cast<float*>(ctx->float_ws);
   p.sinks = args->sinks;
   p.num_qo_heads = ctx->num_qo_heads;

@@ -12,6 +12,7 @@ namespace pod {
 constexpr int kHeadDim = 128;
 constexpr int kThreads = 512;          // 8 wave64 per workgroup (2 per SIMD)
 constexpr int kTileRows = 256;         // rows of a query-tile item (8 waves x 32)
+constexpr int kTileKeys = 64;          // keys per block of a query tile
 constexpr int kMaxGroup = 128;         // largest supported num_qo_heads / num_kv_heads
 constexpr int kChunkRows = 32;         // max rows of a key-chunk item (one MFMA column block)
 constexpr int kItemWords = 8;
@@ -19,6 +20,19 @@ constexpr int kReqWords = 4;
 constexpr int kGroupWords = 4;
 constexpr int kNumXcds = 8;            // MI355X: 8 accelerator dies, 32 CUs each
 constexpr int kSlotFloats = kChunkRows * kHeadDim + kChunkRows;   // partial O + LSE
+constexpr int kWgWords = 8;            // per-workgroup list header
+constexpr int kBlockWords = 4;         // query-tile block-table entry
+constexpr int kMaxSinkHeads = 1024;    // sinks staged in LDS by the query tiles
+constexpr int kMaxKvHeads = 16384;     // kv head index fits the block-table entry
+constexpr int kMaxTilesPerWg = 65536;  // tile index fits the block-table entry
+
+// Block-table entry of a workgroup's query-tile stream:
+//   {first key of the block, last key of its item, first page of the request, meta}
+// meta: bit 31 first block of its item, bit 30 role, bits 16..29 kv head,
+// bits 0..15 index of the item among the workgroup's query tiles.
+constexpr uint32_t kEntFirst = 1u << 31;
+constexpr int kEntRoleShift = 30;
+constexpr int kEntKvhShift = 16;
 
 // item flags
 constexpr int kFlagRole = 1;           // bit 0: 0 prefill, 1 decode
@@ -44,8 +58,14 @@ struct Params {
   RoleParams role[2];
   const int32_t* reqs;
   const int32_t* items;
+  const int32_t* wgs;       // per workgroup: {first item, tiles, chunks, first block, blocks,
+                            //   chunks first, prefill tiles, prefill blocks}
+  const int32_t* blocks;    // query-tile block tables
   const int32_t* groups;
   int32_t* counters;
+  int32_t* queue;           // {next pool item, workgroups done}; zero between launches
+  int32_t pool_first;       // shared key-chunk pool: items [pool_first, pool_first + pool_count)
+  int32_t pool_count;
   float* partials;
   const float* sinks;       // nullptr = no sinks
   int32_t num_qo_heads;

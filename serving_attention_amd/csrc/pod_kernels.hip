@@ -73,7 +73,6 @@ struct Dt<_Float16> {
 
 constexpr int kRowBytes = kHeadDim * 2;       // one kv head's K row (16-bit types)
 constexpr int kVRowBytes = kRowBytes + 64;    // V rows are padded by 64 bytes
-constexpr int kTileKeys = 64;                 // keys per LDS block of a query tile
 constexpr int kStepKeys = 32;                 // keys per wave step of a key chunk
 // Query-tile K block: row R sits in 1040-byte group R % 16 at slot R / 16, so
 // each group is one lane-contiguous direct-to-LDS load of 4 rows, the 16
@@ -207,9 +206,21 @@ struct RoleView {
   int causal, window_left;
 };
 
-__device__ __forceinline__ RoleView pick_role(const Params& p, int role, int kvh) {
-  const RoleParams& a = p.role[0];
-  const RoleParams& b = p.role[1];
+// Kernel parameters are read in place from the kernarg segment (through the
+// scalar unit) where they are used, rather than all loaded at entry and held
+// in scalar registers for the whole launch.
+using PArg = const __attribute__((address_space(4))) Params&;
+// the same reference, opaque to the compiler: loads through it stay where they
+// are written (not hoisted out of the loop that contains them)
+__device__ __forceinline__ PArg reload(PArg p) {
+  const __attribute__((address_space(4))) Params* q = &p;
+  asm volatile("" : "+s"(q));
+  return *q;
+}
+
+__device__ __forceinline__ RoleView pick_role(PArg p, int role, int kvh) {
+  const __attribute__((address_space(4))) RoleParams& a = p.role[0];
+  const __attribute__((address_space(4))) RoleParams& b = p.role[1];
   RoleView r;
   r.q = role ? b.q : a.q;
   r.q_st = role ? b.q_st : a.q_st;
@@ -231,11 +242,11 @@ __device__ __forceinline__ RoleView pick_role(const Params& p, int role, int kvh
 }
 
 // Physical page of logical key `key` and the byte offset of its row in the pool.
-__device__ __forceinline__ uint32_t page_of(const RoleView& r, const Params& p, int page_start, int key) {
+__device__ __forceinline__ uint32_t page_of(const RoleView& r, PArg p, int page_start, int key) {
   const int pg = p.page_shift >= 0 ? (key >> p.page_shift) : key / p.page_size;
   return r.indices ? (uint32_t)r.indices[page_start + pg] : (uint32_t)(page_start + pg);
 }
-__device__ __forceinline__ uint64_t row_off(const RoleView& r, const Params& p, uint32_t page, int key) {
+__device__ __forceinline__ uint64_t row_off(const RoleView& r, PArg p, uint32_t page, int key) {
   const int slot = p.page_shift >= 0 ? (key & (p.page_size - 1)) : key % p.page_size;
   return (uint64_t)page * r.kv_sp_b + (uint32_t)slot * r.kv_st_b;
 }
@@ -321,12 +332,14 @@ __device__ __forceinline__ void softmax_step(f32x16 (&s)[NB], float sl2, float& 
 }
 
 // ----------------------------------------------------------------------------
-// Query tile: up to 256 rows (tokens x group heads) of one request and kv head,
-// keys [kv_begin, kv_end) in 64-key blocks; wave w owns rows 32w + [0, 32).
-// K/V blocks go straight from HBM/L2 to LDS (16-byte direct loads) through a
-// ring of 4 slots, three blocks ahead of the one computed, with one barrier per
-// block; the eight waves share every block (two per SIMD, so one wave's
-// exponentials run beside the other's MFMAs).
+// Query tiles: up to 256 rows (tokens x group heads) of one request and kv head
+// over the item's keys in 64-key blocks; wave w owns rows 32w + [0, 32). A
+// workgroup runs all of its query tiles as one stream of blocks (the planner's
+// block table): K/V blocks go straight from HBM/L2 to LDS (16-byte direct
+// loads) through a ring of 4 slots, two blocks ahead of the one computed, so
+// the next tile's page ids and first blocks are in flight while the current
+// tile finishes. The eight waves share every block (two per SIMD, so one
+// wave's exponentials run beside the other's MFMAs).
 template <bool kPow2>
 struct PageMap {
   int shift, mask, size;
@@ -334,77 +347,111 @@ struct PageMap {
   __device__ __forceinline__ int slot(int key) const { return kPow2 ? key & mask : key % size; }
 };
 
+// Read-only plan words through the scalar unit (the plan is constant during
+// a launch).
+using CI32 = const __attribute__((address_space(4))) int32_t;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+using CI32x4 = const __attribute__((address_space(4))) i32x4;
+__device__ __forceinline__ CI32* plan_words(const int32_t* p) { return (CI32*)p; }
+
+// one query-tile item, wave-uniform
+struct TileDesc {
+  int role, kvh, tok0, ntok, kv_end, qo_start, qo_len, kv_len;
+};
+__device__ __forceinline__ TileDesc tile_desc(PArg p, CI32* items, int idx) {
+  CI32* it = items + idx * kItemWords;
+  TileDesc d;
+  d.role = it[0] & kFlagRole;
+  d.kvh = it[2];
+  d.tok0 = it[3];
+  d.ntok = it[4];
+  d.kv_end = it[6];
+  CI32* rq = plan_words(p.reqs) + it[1] * kReqWords;
+  d.qo_start = rq[0];
+  d.qo_len = rq[1];
+  d.kv_len = rq[2];
+  return d;
+}
+
+
 template <typename T, bool kPow2>
-__device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg, int kvh, int tok0,
-                          int ntok, int kv_begin, int kv_end, char* ring, char* idring) {
+__device__ void tile_stream(PArg p, int role, const int32_t* titems, const int32_t* tab,
+                            int nv, char* ring, char* idring, float* sink_lds) {
   using V8 = typename Dt<T>::v8;
+  CI32* ctab = plan_words(tab);
+  CI32* citems = plan_words(titems);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
   const int g = p.group_size;
-  const int rows = ntok * g;
   const int row = wave * 32 + r32;
-  const bool row_ok = row < rows;
-  const bool active = wave * 32 < rows;   // wave-uniform: the wave has rows
-  const int tok = tok0 + (row_ok ? row / g : 0);
-  const int head = kvh * g + (row_ok ? row % g : 0);
+  const bool second = wave >= kWaves / 2;   // wave-uniform: the V-first half
+  const PageMap<kPow2> pm{p.page_shift, p.page_size - 1, p.page_size};
+  // the role's K/V pools (kv head 0), page table and strides: all the block
+  // loads need; the rest of the role is read again at item boundaries
+  const RoleView r = pick_role(p, role, 0);
+  const char* const kpool = r.k;
+  const char* const vpool = r.v;
+  const bool paged = r.indices != nullptr;
+  // page-id loads read the page table, or word 0 of the request table (unused)
+  const int32_t* const id_src = paged ? r.indices : p.reqs;
+  const uint32_t kv_sp = r.kv_sp_b, kv_st = r.kv_st_b;
+  const uint32_t kv_sh = role ? p.role[1].kv_sh_b : p.role[0].kv_sh_b;
 
-  V8 qreg[8];
-  load_q<T>(qreg, r, row_ok, rg.qo_start + tok, head, hi);
-
-  const int pdiag = rg.kv_len - rg.qo_len + tok;
-  const int key_hi = min(r.causal ? pdiag : rg.kv_len - 1, kv_end - 1);
-  const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
-  const RowMask rm = row_mask(key_lo, key_hi);
+  // block v's entry (blocks past the end repeat the last one), one 16-byte
+  // scalar load; each pass loads the entries it needs at its start and carries
+  // those of the blocks it computes from earlier passes
+  struct Ent {
+    int kb, kl, ps;
+    uint32_t meta;
+  };
+  auto ent = [&](int v) {
+    const i32x4 e = reinterpret_cast<CI32x4*>(ctab)[min(v, nv - 1)];
+    return Ent{e[0], e[1], e[2], (uint32_t)e[3]};
+  };
+  auto is_first = [](const Ent& e) { return (e.meta & kEntFirst) != 0; };
+  auto item_idx = [](const Ent& e) { return (int)(e.meta & 0xffff); };
 
   // Direct loads: wave w fills groups 2w+u (u = 0, 1) of K and of V; group i
   // holds rows i + 16 (lane / 16), lane & 15 is the 16-byte slot. K row R sits at
-  // (R % 16) * 1024 + (R / 16) * 256 with XOR-swizzled chunks; V row R at
-  // (R % 16) * 1088 + (R / 16) * 256 (1088-byte groups: the 4 consecutive rows of
-  // a transpose read land 16 banks apart). Rows past kv_end repeat row
-  // kv_end - 1 (finite values the mask sends to -inf), and blocks past the end
-  // load that row too, so every block issues the same loads.
+  // (R % 16) * 1040 + (R / 16) * 256, V row R at (R % 16) * 1088 + (R / 16) * 256.
+  // Rows past the item's last key repeat that key (finite values the mask sends
+  // to -inf), and blocks past the end of the stream load the last block again,
+  // so every iteration issues the same loads.
   const int lq = lane >> 4, lslot = lane & 15;
-  const int nblk = kv_begin < kv_end ? (kv_end - kv_begin + kTileKeys - 1) / kTileKeys : 0;
-  const PageMap<kPow2> pm{p.page_shift, p.page_size - 1, p.page_size};
-  const int kv_last = kv_end - 1;
-  const char* kbase[2];
   int rr[2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    rr[u] = 2 * wave + u + 16 * lq;
-    kbase[u] = r.k + (lslot << 4);
-  }
-  const char* vbase = r.v + (lslot << 4);
+  for (int u = 0; u < 2; ++u) rr[u] = 2 * wave + u + 16 * lq;
   // Page ids stream through a per-wave LDS ring too (lane l holds the page of
   // key kb + l); without a page table the loads read word 0 of the request
   // table and the identity page is used instead.
-  const bool has_ip = r.indices != nullptr;
-  const int32_t* ip = has_ip ? r.indices + rg.page_start : p.reqs;
-  auto idslot = [&](int blk) { return idring + (blk & (kRingSlots - 1)) * kIdSlot + wave * 256; };
-  auto slot = [&](int blk) { return ring + (blk & (kRingSlots - 1)) * kTileBuf; };
-  auto load_ids = [&](int blk) {
-    const uint32_t pl = (uint32_t)pm.page(min(kv_begin + blk * kTileKeys + lane, kv_last));
-    lds_dma4(ip + (has_ip ? pl : 0u), idslot(blk));
+  auto idslot = [&](int v) { return idring + (v & (kRingSlots - 1)) * kIdSlot + wave * 256; };
+  auto slot = [&](int v) { return ring + (v & (kRingSlots - 1)) * kTileBuf; };
+  auto load_ids = [&](int v, const Ent& e) {
+    const int kb = e.kb, kl = e.kl, ps = e.ps;
+    const uint32_t pl = (uint32_t)pm.page(min(kb + lane, kl));
+    lds_dma4(id_src + (paged ? ps + pl : 0u), idslot(v));
   };
   int32_t pid[2];
-  auto read_ids = [&](int blk) {
+  auto read_ids = [&](int v) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) pid[u] = *reinterpret_cast<const int32_t*>(idslot(blk) + rr[u] * 4);
+    for (int u = 0; u < 2; ++u) pid[u] = *reinterpret_cast<const int32_t*>(idslot(v) + rr[u] * 4);
   };
-  // the K and V loads of the wave's row group u of block blk
-  auto dma_rows = [&](int blk, int u) {
-    const int kb = kv_begin + blk * kTileKeys;
-    char* dst = slot(blk);
-    const int key = min(kb + rr[u], kv_last);
-    const uint32_t page = has_ip ? (uint32_t)pid[u] : (uint32_t)(rg.page_start + pm.page(key));
-    const uint64_t ro = (uint64_t)page * r.kv_sp_b + (uint32_t)pm.slot(key) * r.kv_st_b;
-    lds_dma16(kbase[u] + ro, dst + (2 * wave + u) * kTileKGroup);
-    lds_dma16(vbase + ro, dst + kTileKBytes + (2 * wave + u) * kTileVGroup);
+  // the K and V loads of the wave's row group u of block v
+  auto dma_rows = [&](int v, int u, const Ent& e) {
+    const int kb = e.kb, kl = e.kl, ps = e.ps;
+    const uint32_t kvh = (e.meta >> kEntKvhShift) & 0x3fff;
+    const int key = min(kb + rr[u], kl);
+    const uint32_t page = paged ? (uint32_t)pid[u] : (uint32_t)(ps + pm.page(key));
+    const uint64_t ro = (uint64_t)page * kv_sp + (uint32_t)pm.slot(key) * kv_st +
+                        (uint64_t)kvh * kv_sh + (lslot << 4);
+    char* dst = slot(v);
+    lds_dma16(kpool + ro, dst + (2 * wave + u) * kTileKGroup);
+    lds_dma16(vpool + ro, dst + kTileKBytes + (2 * wave + u) * kTileVGroup);
   };
-  auto dma_block = [&](int blk) {
-    dma_rows(blk, 0);
-    dma_rows(blk, 1);
+  auto dma_block = [&](int v, const Ent& e) {
+    dma_rows(v, 0, e);
+    dma_rows(v, 1, e);
   };
 
   // K operand: lane reads row h*32 + key_row(r32), chunk hi*8 + c, at
@@ -416,11 +463,79 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
   const int vlane = kTileKBytes + (8 * (vg >> 1) + (vi >> 2)) * kTileVGroup +
                     (16 * (vg & 1) + 4 * (vi & 3)) * 2;
 
+  // entries of the blocks computed next (block t and t + 1 of a pass)
+  Ent ea = ent(0), eb = ent(1);
+  // the item whose softmax state (rm, m, l, o) is live
+  int cur = item_idx(ea);
+  V8 qreg[8];
   f32x16 o[4];
+  float m = kNegInf, l = 0.f, sl2 = 0.f;
+  RowMask rm;
+  // this lane's row of item d: token, qo head; false past the item's rows
+  auto geom = [&](const TileDesc& d, int& tok, int& head) {
+    const bool ok = row < d.ntok * g;
+    tok = d.tok0 + (ok ? row / g : 0);
+    head = d.kvh * g + (ok ? row % g : 0);
+    return ok;
+  };
+  // item i of the list, and its role, read again where they are needed
+  // a use of the query registers: the compiler waits here for the query loads
+  // (vmcnt(0), with every load issued before them), so no wait for them is
+  // left in the loop.
+  auto query_landed = [&]() {
+    asm volatile("" ::"v"(qreg[0]), "v"(qreg[1]), "v"(qreg[2]), "v"(qreg[3]), "v"(qreg[4]),
+                 "v"(qreg[5]), "v"(qreg[6]), "v"(qreg[7]));
+  };
+  auto load_query = [&](int i) {
+    PArg q = reload(p);
+    const TileDesc d = tile_desc(q, citems, i);
+    int tok, head;
+    const bool ok = geom(d, tok, head);
+    load_q<T>(qreg, pick_role(q, role, 0), ok, d.qo_start + tok, head, hi);
+  };
+  auto setup = [&](int i) {
+    PArg q = reload(p);
+    const TileDesc d = tile_desc(q, citems, i);
+    const RoleView r = pick_role(q, role, 0);
+    int tok, head;
+    geom(d, tok, head);
+    const int pdiag = d.kv_len - d.qo_len + tok;
+    const int key_hi = min(r.causal ? pdiag : d.kv_len - 1, d.kv_end - 1);
+    const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
+    rm = row_mask(key_lo, key_hi);
+    sl2 = r.scale_log2;
+    m = kNegInf;
+    l = 0.f;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) o[b] = f32x16{};
-  float m = kNegInf, l = 0.f;
-  const float sl2 = r.scale_log2;
+    for (int b = 0; b < 4; ++b) o[b] = f32x16{};
+  };
+  // normalise (sink folded into the denominator) and store O and the LSE of item d
+  auto finish = [&](int i) {
+    PArg q = reload(p);
+    const TileDesc d = tile_desc(q, citems, i);
+    const RoleView r = pick_role(q, role, 0);
+    int tok, head;
+    const bool ok = geom(d, tok, head);
+    const float lt = xhalf_sum(l);
+    if (ok) {
+      const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
+      float den = lt;
+      if (q.sinks) den += fast_exp2(sink_lds[head] * kLog2e - mu2);
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      T* op = reinterpret_cast<T*>(r.out) + (int64_t)(d.qo_start + tok) * r.o_st + (int64_t)head * r.o_sh;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          typename Dt<T>::v4 w;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) w[c] = (T)(o[db][4 * a + c] * inv);
+          *reinterpret_cast<u32x2*>(op + db * 32 + acc_d(4 * a, hi)) = __builtin_bit_cast(u32x2, w);
+        }
+      if (r.lse && hi == 0)
+        r.lse[(int64_t)(d.qo_start + tok) * q.num_qo_heads + head] = lt > 0.f ? mu2 + fast_log2(lt) : kNegInf;
+    }
+  };
 
   // Each block b is two phases of a wave:
   //   M: the score MFMAs of block b (S_b, 16, K from LDS slot b) and the P.V
@@ -476,16 +591,20 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
     }
   };
-  auto v_phase = [&](int b) {
+  auto v_phase = [&](int kb) {
     __builtin_amdgcn_s_setprio(1);
-    const int kb = kv_begin + b * kTileKeys;
     if (__any((unsigned)(kb - rm.lo) > rm.span || (unsigned)(kb + kTileKeys - 1 - rm.lo) > rm.span)) {
+      // key of accumulator j = kb + 8 hi + (its constant part); the lane part
+      // is opaque so that the 32 key offsets are not held in registers
+      int base = 8 * hi;
+      asm volatile("" : "+v"(base));
+      base += kb - rm.lo;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const int kidx = kb + h * 32 + acc_key(j, hi);
-          s[h][j] = ((unsigned)(kidx - rm.lo) <= rm.span) ? s[h][j] : kNegInf;
+          const int kidx = base + h * 32 + acc_key(j, 0);
+          s[h][j] = ((unsigned)kidx <= rm.span) ? s[h][j] : kNegInf;
         }
     }
     update_max<2>(s, sl2, m, l, o);
@@ -495,28 +614,34 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Block b streams into ring slot b % 4 and its page ids into id slot b % 4.
+  // Block v streams into ring slot v % 4 and its page ids into id slot v % 4.
   // Iteration t reads slots t-1 and t and, between its two turns, issues the
   // K/V loads of block t+2 (4 loads, into the slot of block t-2) and then the ids
   // of block t+6 (1 load), and moves the ids of block t+3 to registers. The
-  // prologue issues what iterations -2 and -1 would have.
-  const bool second = wave >= kWaves / 2;   // wave-uniform: the V-first half
-  if (nblk > 0) {
-    load_ids(0);
-    load_ids(1);
-    load_ids(2);
-    load_ids(3);
-    wait_vm<3>();
-    read_ids(0);
-    dma_block(0);
-    load_ids(4);
-    wait_vm<7>();
-    read_ids(1);
-    dma_block(1);
-    load_ids(5);
-    wait_vm<11>();
-    read_ids(2);
+  // prologue issues what iterations -2 and -1 would have, after the sinks (LDS
+  // copy, for the tiles' final normalisation) and the first tile's query.
+  setup(cur);
+  load_query(cur);
+  if (p.sinks) {
+    for (int c = wave; c * 64 < p.num_qo_heads; c += kWaves)
+      lds_dma4(p.sinks + min(c * 64 + lane, p.num_qo_heads - 1), (char*)sink_lds + c * 256);
   }
+  load_ids(0, ea);
+  load_ids(1, eb);
+  load_ids(2, ent(2));
+  load_ids(3, ent(3));
+  wait_vm<3>();
+  read_ids(0);
+  dma_block(0, ea);
+  load_ids(4, ent(4));
+  wait_vm<7>();
+  read_ids(1);
+  dma_block(1, eb);
+  load_ids(5, ent(5));
+  wait_vm<11>();
+  read_ids(2);
+  query_landed();
+
   // iteration t: wait for block t, then issue block t+2's loads
   auto top = [&](int t) {
     // block t landed (and the ids of block t+3, issued before it); the 6 loads
@@ -524,97 +649,141 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
     wait_vm<6>();
     ring_barrier();
   };
-  // Block t+2's loads go out in two parts, one at the start of each turn of
-  // the wave (all eight waves issuing all their loads at one point queue up
-  // behind each other); then the ids of block t+6.
-  auto ids = [&](int t) {
-    load_ids(t + 6);
-    read_ids(t + 3);
-  };
-  // Iteration t: waves 0-3 run M(t) then V(t), waves 4-7 V(t-1) then M(t),
-  // where M(t) = S_t (t < nblk) and P.V of block t-1 (t > 0). Each half runs
-  // its own straight-line loop; both pass the same 2 (nblk + 1) barriers.
-  if (nblk > 0) {
-    if (!active) {
-      for (int t = 0; t <= nblk; ++t) {
-        top(t);
-        dma_rows(t + 2, 0);
-        ring_barrier();
-        dma_rows(t + 2, 1);
-        ids(t);
-      }
-    } else if (!second) {
+  // Item boundaries: block t opens a new item (first block): after the M turn
+  // that ends the previous item's P.V, that item is normalised and stored and
+  // the new one's state reset (placed so that the stores never sit between a
+  // block's loads and the wait for them). Block t closes its item (the next
+  // block opens one): after the M turn of S_t the next item's query goes to the
+  // registers and is waited for at once (with every load issued before it):
+  // one load latency per item, and no wait on the query in the other passes.
+  if (!second) {
+    // waves 0-3, iteration t: M(t), barrier, V(t)
+    // e2, e6: entries of blocks t+2 and t+6, loaded one pass ahead
+    Ent e2 = ent(2), e6 = ent(6);
+    {
       top(0);
-      dma_rows(2, 0);
+      dma_rows(2, 0, e2);
       m_s(0);
       ring_barrier();
-      dma_rows(2, 1);
-      ids(0);
-      v_phase(0);
-      for (int t = 1; t < nblk; ++t) {
-        top(t);
-        dma_rows(t + 2, 0);
-        m_both(t);
-        ring_barrier();
-        dma_rows(t + 2, 1);
-        ids(t);
-        v_phase(t);
+      dma_rows(2, 1, e2);
+      load_ids(6, e6);
+      read_ids(3);
+      if (nv > 1 && is_first(eb)) {
+        load_query(item_idx(eb));
+        query_landed();
       }
-      top(nblk);
-      dma_rows(nblk + 2, 0);
-      m_pv(nblk - 1);
-      ring_barrier();
-      dma_rows(nblk + 2, 1);
-      ids(nblk);
-    } else {
-      top(0);
-      dma_rows(2, 0);
-      ring_barrier();
-      m_s(0);
-      dma_rows(2, 1);
-      ids(0);
-      for (int t = 1; t < nblk; ++t) {
-        top(t);
-        dma_rows(t + 2, 0);
-        v_phase(t - 1);
-        ring_barrier();
-        m_both(t);
-        dma_rows(t + 2, 1);
-        ids(t);
-      }
-      top(nblk);
-      dma_rows(nblk + 2, 0);
-      v_phase(nblk - 1);
-      ring_barrier();
-      m_pv(nblk - 1);
-      dma_rows(nblk + 2, 1);
-      ids(nblk);
+      const Ent n2 = ent(3), n6 = ent(7);
+      v_phase(ea.kb);
+      ea = eb;
+      eb = e2;
+      e2 = n2;
+      e6 = n6;
     }
+    for (int t = 1; t < nv; ++t) {
+      const bool bnd = is_first(ea);
+      const bool nq = t + 1 < nv && is_first(eb);
+      top(t);
+      dma_rows(t + 2, 0, e2);
+      m_both(t);
+      ring_barrier();
+      if (bnd) {
+        finish(cur);
+        cur = item_idx(ea);
+        setup(cur);
+      }
+      dma_rows(t + 2, 1, e2);
+      load_ids(t + 6, e6);
+      read_ids(t + 3);
+      if (nq) {
+        load_query(item_idx(eb));
+        query_landed();
+      }
+      // next pass's entries: issued where no LDS wait follows until the next
+      // pass (scalar and LDS loads share one counter)
+      const Ent n2 = ent(t + 3), n6 = ent(t + 7);
+      v_phase(ea.kb);
+      ea = eb;
+      eb = e2;
+      e2 = n2;
+      e6 = n6;
+    }
+    {
+      top(nv);
+      dma_rows(nv + 2, 0, e2);
+      m_pv(nv - 1);
+      ring_barrier();
+      dma_rows(nv + 2, 1, e2);
+      load_ids(nv + 6, e6);
+      read_ids(nv + 3);
+    }
+  } else {
+    // waves 4-7, iteration t: V(t-1), barrier, M(t); the loop below runs from
+    // the M turn of t to the V turn of t (so a query issued after M(t) is
+    // waited for at the end of the same pass)
+    // entering pass t: ea, eb, ec = entries of blocks t, t+1, t+2; e3, e6 =
+    // entries of blocks t+3 and t+6, loaded one pass ahead
+    Ent ec, e3, e6;
+    {
+      const Ent e2 = ent(2);
+      e3 = ent(3);
+      e6 = ent(6);
+      top(0);
+      dma_rows(2, 0, e2);
+      ring_barrier();
+      m_s(0);
+      dma_rows(2, 1, e2);
+      load_ids(6, e6);
+      read_ids(3);
+      top(1);
+      dma_rows(3, 0, e3);
+      if (nv > 1 && is_first(eb)) {
+        load_query(item_idx(eb));
+        query_landed();
+      }
+      const Ent n3 = ent(4), n6 = ent(7);
+      v_phase(ea.kb);
+      ring_barrier();
+      ea = eb;
+      eb = e2;
+      ec = e3;
+      e3 = n3;
+      e6 = n6;
+    }
+    for (int t = 1; t < nv; ++t) {
+      const bool bnd = is_first(ea);
+      const bool nq = t + 1 < nv && is_first(eb);
+      m_both(t);
+      dma_rows(t + 2, 1, ec);
+      load_ids(t + 6, e6);
+      read_ids(t + 3);
+      top(t + 1);
+      dma_rows(t + 3, 0, e3);
+      if (bnd) {
+        finish(cur);
+        cur = item_idx(ea);
+        setup(cur);
+      }
+      if (nq) {
+        load_query(item_idx(eb));
+        query_landed();
+      }
+      const Ent n3 = ent(t + 4), n6 = ent(t + 7);
+      v_phase(ea.kb);
+      ring_barrier();
+      ea = eb;
+      eb = ec;
+      ec = e3;
+      e3 = n3;
+      e6 = n6;
+    }
+    m_pv(nv - 1);
+    dma_rows(nv + 2, 1, ec);
+    load_ids(nv + 6, ent(nv + 6));
+    read_ids(nv + 3);
   }
   // drain the loads of blocks past the end before the LDS is reused
   wait_vm<0>();
-  l = xhalf_sum(l);
-
-  if (row_ok) {
-    const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
-    float den = l;
-    if (p.sinks) den += fast_exp2(p.sinks[head] * kLog2e - mu2);
-    const float inv = den > 0.f ? 1.f / den : 0.f;
-    T* op = reinterpret_cast<T*>(r.out) + (int64_t)(rg.qo_start + tok) * r.o_st +
-            (int64_t)head * r.o_sh;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        typename Dt<T>::v4 w;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) w[c] = (T)(o[db][4 * a + c] * inv);
-        *reinterpret_cast<u32x2*>(op + db * 32 + acc_d(4 * a, hi)) = __builtin_bit_cast(u32x2, w);
-      }
-    if (r.lse && hi == 0)
-      r.lse[(int64_t)(rg.qo_start + tok) * p.num_qo_heads + head] =
-          l > 0.f ? mu2 + fast_log2(l) : kNegInf;
-  }
+  finish(cur);
 }
 
 // ----------------------------------------------------------------------------
@@ -626,10 +795,14 @@ __device__ void tile_item(const Params& p, const RoleView& r, const RowGeom& rg,
 // and the page indices are fetched one step further ahead.
 // Wave states merge in LDS; split chunks merge through the float workspace.
 template <typename T>
-__device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg, int kvh,
+__device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowGeom& rg, int kvh,
                            int kv_begin, int kv_end, int split, int grp, char* lds) {
   using V8 = typename Dt<T>::v8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the thread index, opaque to the compiler so that nothing derived from it
+  // is computed once for all items of the workgroup and held in registers
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
   const int g = p.group_size;
   const int rows = rg.qo_len * g;
@@ -755,8 +928,8 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   __syncthreads();
 
   // final stage on the first 256 threads: row threadIdx / 8, 16 dims each
-  const int frow = (threadIdx.x >> 3) & 31, d0 = (threadIdx.x & 7) * 16;
-  const bool fok = threadIdx.x < 256 && frow < rows;
+  const int frow = (tid >> 3) & 31, d0 = (tid & 7) * 16;
+  const bool fok = tid < 256 && frow < rows;
   const int ftok = fok ? frow / g : 0;
   const int fhead = kvh * g + (fok ? frow % g : 0);
   const int64_t out_row = (int64_t)(rg.qo_start + ftok);
@@ -791,7 +964,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
       }
       reinterpret_cast<u32x4*>(op)[0] = __builtin_bit_cast(u32x4, w0);
       reinterpret_cast<u32x4*>(op)[1] = __builtin_bit_cast(u32x4, w1);
-      if (lse_p && (threadIdx.x & 7) == 0) *lse_p = lse_r;
+      if (lse_p && (tid & 7) == 0) *lse_p = lse_r;
     } else {
       const int first_slot = p.groups[grp * kGroupWords + 1];
       float* slot = p.partials + (int64_t)(first_slot + split) * kSlotFloats;
@@ -801,7 +974,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
       for (int i = 0; i < 4; ++i)
         dst[i] = make_float4(vals[4 * i] * inv, vals[4 * i + 1] * inv, vals[4 * i + 2] * inv,
                              vals[4 * i + 3] * inv);
-      if ((threadIdx.x & 7) == 0) slot[kChunkRows * kHeadDim + frow] = lse_r;
+      if ((tid & 7) == 0) slot[kChunkRows * kHeadDim + frow] = lse_r;
     }
   }
   if (grp < 0) return;
@@ -811,7 +984,7 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
   const int first_slot = p.groups[grp * kGroupWords + 1];
   __threadfence();
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const int prev = atomicAdd(&p.counters[grp], 1);
     *sm_flag = (prev == n_splits - 1);
   }
@@ -854,32 +1027,80 @@ __device__ void chunk_item(const Params& p, const RoleView& r, const RowGeom& rg
     }
     reinterpret_cast<u32x4*>(op)[0] = __builtin_bit_cast(u32x4, w0);
     reinterpret_cast<u32x4*>(op)[1] = __builtin_bit_cast(u32x4, w1);
-    if (lse_p && (threadIdx.x & 7) == 0) *lse_p = L;
+    if (lse_p && (tid & 7) == 0) *lse_p = L;
   }
-  if (threadIdx.x == 0) atomicExch(&p.counters[grp], 0);
+  if (tid == 0) atomicExch(&p.counters[grp], 0);
 }
 
+// One persistent workgroup per CU runs its static list from the plan: its key
+// chunks one after another, and its query tiles as one block stream (chunks
+// first or last, as the plan says). Then it takes key chunks from the shared
+// pool, one at a time through an atomic counter, until the pool is empty; the
+// last workgroup to find it empty puts the counters back to zero for the next
+// launch.
 template <typename T>
-__global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params p) {
-  // the query tile's ring slots, or one 18 KB part per key-chunk wave
+__global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
+  PArg p = *(const __attribute__((address_space(4))) Params*)__builtin_amdgcn_kernarg_segment_ptr();
+  // the query tiles' ring slots, or one 18 KB part per key-chunk wave
   __shared__ __attribute__((aligned(16))) char lds[kLdsMain];
-  // page-id ring of the query tile: 4 slots x 8 waves x 64 words
+  // page-id ring of the query tiles: 4 slots x 8 waves x 64 words
   __shared__ __attribute__((aligned(16))) char ids[kRingSlots * kIdSlot];
-  const int32_t* it = p.items + (int64_t)blockIdx.x * kItemWords;
-  const int flags = it[0];
-  if (flags < 0) return;
-  const int role = flags & kFlagRole;
-  const int req = it[1], kvh = it[2], tok0 = it[3], ntok = it[4];
-  const int kv_begin = it[5], kv_end = it[6], grp = it[7];
-  const RoleView r = pick_role(p, role, kvh);
-  const int32_t* rq = p.reqs + req * kReqWords;
-  RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
-  if (flags & kFlagChunk)
+  // sink logits for the query tiles' normalisation
+  __shared__ __attribute__((aligned(16))) float sink_lds[kMaxSinkHeads];
+  __shared__ int pool_slot;
+  CI32* wg = plan_words(p.wgs) + blockIdx.x * kWgWords;
+  const int first_item = wg[0], n_tiles = wg[1], n_chunks = wg[2];
+  const int first_blk = wg[3], n_blk = wg[4];
+  const bool chunks_first = wg[5] != 0;
+  auto run_chunk = [&](int idx) __attribute__((always_inline)) {
+    CI32* it = plan_words(p.items) + idx * kItemWords;
+    const int flags = it[0];
+    const int kvh = it[2], kv_begin = it[5], kv_end = it[6], grp = it[7];
+    const RoleView r = pick_role(p, flags & kFlagRole, kvh);
+    CI32* rq = plan_words(p.reqs) + it[1] * kReqWords;
+    const RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
     chunk_item<T>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds);
-  else if (p.page_shift >= 0)
-    tile_item<T, true>(p, r, rg, kvh, tok0, ntok, kv_begin, kv_end, lds, ids);
-  else
-    tile_item<T, false>(p, r, rg, kvh, tok0, ntok, kv_begin, kv_end, lds, ids);
+  };
+  auto run_chunks = [&]() {
+    for (int j = 0; j < n_chunks; ++j) {
+      __syncthreads();   // the previous item is done with the LDS
+      run_chunk(first_item + n_tiles + j);
+    }
+  };
+  if (chunks_first) run_chunks();
+  if (n_tiles > 0) {
+    __syncthreads();
+    const int32_t* ti = p.items + (int64_t)first_item * kItemWords;
+    const int32_t* tb = p.blocks + (int64_t)first_blk * kBlockWords;
+    // one block stream per role: the prefill tiles, then the decode tiles
+    const int pre_blk = wg[7];
+    for (int role = 0; role < 2; ++role) {
+      const int b0 = role ? pre_blk : 0, nb = role ? n_blk - pre_blk : pre_blk;
+      if (nb == 0) continue;
+      if (role && pre_blk) __syncthreads();
+      if (p.page_shift >= 0)
+        tile_stream<T, true>(p, role, ti, tb + (int64_t)b0 * kBlockWords, nb, lds, ids, sink_lds);
+      else
+        tile_stream<T, false>(p, role, ti, tb + (int64_t)b0 * kBlockWords, nb, lds, ids, sink_lds);
+    }
+  }
+  if (!chunks_first) run_chunks();
+  if (p.pool_count > 0) {
+    for (;;) {
+      __syncthreads();   // the previous item is done with the LDS and pool_slot
+      if (threadIdx.x == 0) pool_slot = atomicAdd(p.queue, 1);
+      __syncthreads();
+      const int j = __builtin_amdgcn_readfirstlane(pool_slot);
+      if (j >= p.pool_count) break;
+      run_chunk(p.pool_first + j);
+    }
+    // every workgroup has taken its last (empty) turn before it counts itself
+    // done, so the last one can clear both counters
+    if (threadIdx.x == 0 && atomicAdd(p.queue + 1, 1) == (int)gridDim.x - 1) {
+      atomicExch(p.queue, 0);
+      atomicExch(p.queue + 1, 0);
+    }
+  }
 }
 
 }  // namespace

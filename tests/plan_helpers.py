@@ -48,9 +48,20 @@ def decode_image(img):
     h = img[:_lib.POD_HDR_WORDS]
     assert h[0] == _lib.POD_IMAGE_MAGIC
     n_items, grid, n_reqs, n_groups = int(h[1]), int(h[2]), int(h[3]), int(h[4])
+    n_blocks = int(h[14])
     reqs = img[h[5]:h[5] + 4 * n_reqs].reshape(n_reqs, 4)
-    items = img[h[6]:h[6] + 8 * grid].reshape(grid, 8)
+    items = img[h[6]:h[6] + 8 * n_items].reshape(n_items, 8)
+    wgs = img[h[12]:h[12] + 8 * grid].reshape(grid, 8)
+    blocks = img[h[13]:h[13] + 4 * n_blocks].reshape(n_blocks, 4)
     groups = img[h[7]:h[7] + 4 * n_groups].reshape(n_groups, 4)
     counters = img[h[8]:h[8] + n_groups]
-    return dict(n_items=n_items, grid=grid, reqs=reqs, items=items, groups=groups,
-                counters=counters, n_slots=int(h[9]), slot_floats=int(h[10]), chunk=int(h[11]))
+    wg_of_item = np.full(n_items, -1, np.int64)
+    for w, wg in enumerate(wgs):
+        first, nt, nc = int(wg[0]), int(wg[1]), int(wg[2])
+        wg_of_item[first:first + nt + nc] = w
+    pool_first, pool_count = int(h[15]), int(h[16])
+    queue = img[h[17]:h[17] + 2]
+    return dict(n_items=n_items, grid=grid, reqs=reqs, items=items, wgs=wgs, blocks=blocks,
+                wg_of_item=wg_of_item, groups=groups, counters=counters, n_slots=int(h[9]),
+                slot_floats=int(h[10]), chunk=int(h[11]), pool_first=pool_first,
+                pool_count=pool_count, queue=queue)

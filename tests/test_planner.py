@@ -1,6 +1,7 @@
 """Host planner, driven through pod_plan_compute (no GPU): the work list covers
-every (row, kv head, valid key) exactly once, split groups are consistent,
-items sit on the die their slot maps to, and bad inputs get their error code."""
+every (row, kv head, valid key) exactly once, split groups are consistent, the
+per-workgroup lists partition the items and their block tables match the query
+tiles, and bad inputs get their error code."""
 import numpy as np
 import pytest
 
@@ -78,6 +79,7 @@ def check_coverage(img, roles, hqo, hkv):
             slots.add(s)
     assert slots == set(range(im["n_slots"]))
     assert np.all(im["counters"] == 0)
+    assert np.all(im["queue"] == 0)
     return im
 
 
@@ -133,10 +135,8 @@ def test_tiles_of_one_kv_unit_share_a_die():
     im = decode_image(img)
     die = {}
     for s, it in enumerate(im["items"]):
-        if it[0] == -1:
-            continue
         key = (int(it[1]), int(it[2]))
-        die.setdefault(key, set()).add(s % 8)
+        die.setdefault(key, set()).add(int(im["wg_of_item"][s]) % 8)
     assert all(len(v) == 1 for v in die.values())
 
 
@@ -162,19 +162,106 @@ def test_orders_are_permutations_of_the_same_items():
         assert items == base
 
 
-def test_longest_first_orders_each_die_by_estimated_cost():
-    # the planner's estimates: 40 units per key of a query tile, 26 per key of a key chunk
-    desc, keep = plan_desc(prefill=dict(qo_lens=[300, 50], kv_lens=[700, 60]),
-                           decode=dict(qo_lens=[1] * 9, kv_lens=list(range(100, 1000, 100))),
-                           hqo=8, hkv=2, order=3, decode_chunk=-1)
+def item_cost(it):
+    # the planner's estimates (ns of one workgroup): tiles 1500 + 33 per key, chunks 2500 + 20 per key
+    keys = int(it[6] - it[5])
+    return 2500 + 20 * keys if int(it[0]) & FLAG_CHUNK else 1500 + 33 * keys
+
+
+WORKLOADS = [
+    dict(prefill=dict(qo_lens=[300, 50], kv_lens=[700, 60]),
+         decode=dict(qo_lens=[1] * 9, kv_lens=list(range(100, 1000, 100))), hqo=8, hkv=2),
+    dict(prefill=dict(qo_lens=[2048, 2048], kv_lens=[2048, 2048]),
+         decode=dict(qo_lens=[1] * 128, kv_lens=[2048] * 128), hqo=64, hkv=8, page_size=1),
+    dict(prefill=dict(qo_lens=[4096], kv_lens=[20480], window_left=4096),
+         decode=dict(qo_lens=[4] * 64, kv_lens=[1024 + 500 * i for i in range(64)], window_left=4096),
+         hqo=64, hkv=8),
+    dict(decode=dict(qo_lens=[1, 2], kv_lens=[100, 300]), hqo=64, hkv=1),
+]
+
+
+@pytest.mark.parametrize("order", [0, 1, 2, 3])
+@pytest.mark.parametrize("wl", range(len(WORKLOADS)))
+def test_workgroup_lists(wl, order):
+    """Every item sits in exactly one workgroup list: query tiles first (prefill
+    role, then decode role), then key chunks, each kind heaviest first; within a
+    die the lists are balanced to within one item; the chunks-first flag follows
+    the order policy."""
+    desc, keep = plan_desc(order=order, **WORKLOADS[wl])
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    im = decode_image(img)
+    items, wgs = im["items"], im["wgs"]
+    assert info.grid == 256 and len(wgs) == 256
+    pf, pc = im["pool_first"], im["pool_count"]
+    assert pf + pc == im["n_items"]
+    assert np.all(im["wg_of_item"][:pf] >= 0) and np.all(im["wg_of_item"][pf:] == -1)
+    nxt = 0
+    loads = np.zeros(len(wgs))
+    for w, wg in enumerate(wgs):
+        first, nt, nc, chunks_first, npt = (int(x) for x in (wg[0], wg[1], wg[2], wg[5], wg[6]))
+        assert first == nxt
+        nxt += nt + nc
+        tiles, chunks = items[first:first + nt], items[first + nt:first + nt + nc]
+        assert all(int(t[0]) & FLAG_CHUNK == 0 for t in tiles)
+        assert all(int(c[0]) & FLAG_CHUNK for c in chunks)
+        roles = [int(t[0]) & FLAG_ROLE for t in tiles]
+        assert roles == sorted(roles) and roles.count(0) == npt
+        for part in (tiles[:npt], tiles[npt:], chunks):
+            c = [item_cost(it) for it in part]
+            assert c == sorted(c, reverse=True)
+        loads[w] = sum(item_cost(it) for it in items[first:first + nt + nc])
+        if nt and nc:
+            expect = {0: (w // 8) % 2 == 1, 1: False, 2: True,
+                      3: item_cost(chunks[0]) > item_cost(tiles[0])}[order]
+            assert bool(chunks_first) == expect
+        else:
+            assert chunks_first == 0
+    assert nxt == pf
+    # the shared pool: key chunks only, heaviest first, at most a quarter of
+    # the chunks' estimated cost, and none heavier than a chunk left in a list
+    pool = items[pf:]
+    assert all(int(c[0]) & FLAG_CHUNK for c in pool)
+    pc_cost = [item_cost(c) for c in pool]
+    assert pc_cost == sorted(pc_cost, reverse=True)
+    chunk_costs = [item_cost(c) for c in items if int(c[0]) & FLAG_CHUNK]
+    assert sum(pc_cost) <= 0.25 * sum(chunk_costs) + 1
+    listed = [item_cost(c) for c in items[:pf] if int(c[0]) & FLAG_CHUNK]
+    if pool.size and listed:
+        assert max(pc_cost) <= min(listed)
+    biggest = max(item_cost(it) for it in items)
+    for x in range(8):
+        die = loads[x::8]
+        assert die.max() - die.min() <= biggest
+
+
+@pytest.mark.parametrize("wl", range(len(WORKLOADS)))
+def test_block_tables(wl):
+    """Each workgroup's block table walks its query tiles in list order, 64 keys
+    per block, with the first-block flag, role, kv head and tile index in meta."""
+    desc, keep = plan_desc(**WORKLOADS[wl])
     rc, img, info = compute(desc)
     im = decode_image(img)
-    items = im["items"]
-    grid = len(items)
-    for x in range(8):
-        costs = [(26 if int(it[0]) & FLAG_CHUNK else 40) * int(it[6] - it[5])
-                 for it in items[x::8] if it[0] != -1]
-        assert costs == sorted(costs, reverse=True)
+    items, reqs, blocks = im["items"], im["reqs"], im["blocks"]
+    total = 0
+    for w, wg in enumerate(im["wgs"]):
+        first, nt, fb, nb, npb = int(wg[0]), int(wg[1]), int(wg[3]), int(wg[4]), int(wg[7])
+        assert fb == total
+        exp = []
+        n_pre_blocks = 0
+        for j in range(nt):
+            it = items[first + j]
+            role, kvh, lo, hi = int(it[0]) & FLAG_ROLE, int(it[2]), int(it[5]), int(it[6])
+            ps = int(reqs[int(it[1])][3])
+            for kb in range(lo, hi, 64):
+                meta = (1 << 31 if kb == lo else 0) | (role << 30) | (kvh << 16) | j
+                exp.append((kb, hi - 1, ps, meta))
+                n_pre_blocks += role == 0
+        got = [(int(e[0]), int(e[1]), int(e[2]), int(e[3]) & 0xffffffff) for e in blocks[fb:fb + nb]]
+        assert got == exp
+        assert npb == n_pre_blocks
+        total += nb
+    assert total == len(blocks)
 
 
 def test_workspace_sizes():
@@ -193,6 +280,8 @@ def test_workspace_sizes():
     (dict(dtype=7), _lib.POD_ERR_UNSUPPORTED),
     (dict(hqo=256, hkv=1), _lib.POD_ERR_UNSUPPORTED),
     (dict(order=9), _lib.POD_ERR_INVALID),
+    (dict(hqo=2048, hkv=16, sinks=1), _lib.POD_ERR_UNSUPPORTED),
+    (dict(hqo=32768, hkv=32768), _lib.POD_ERR_UNSUPPORTED),
 ])
 def test_invalid_plan_parameters(case, code):
     args = dict(prefill=dict(qo_lens=[10], kv_lens=[10]), hqo=8, hkv=2)
