@@ -229,7 +229,7 @@ int pod_plan_compute(const pod_plan_desc* desc, int32_t* image, size_t image_cap
  *     [3] n_reqs, [4] n_groups, [5] reqs_off, [6] items_off, [7] groups_off,
  *     [8] counters_off, [9] n_slots, [10] slot_floats, [11] decode_chunk,
  *     [12] wgs_off, [13] blocks_off, [14] n_blocks, [15] pool_first,
- *     [16] pool_count, [17] queue_off.
+ *     [16] pool_count, [17] queue_off, [18] tdesc_off.
  *   reqs[n_reqs][4]: {qo_start, qo_len, kv_len, page_start} per request, prefill
  *     requests first, then decode requests.
  *   items[n_items][8]: {flags, req, kv_head, tok0, ntok, kv_begin, kv_end, group}.
@@ -239,6 +239,8 @@ int pod_plan_compute(const pod_plan_desc* desc, int32_t* image, size_t image_cap
  *     by workgroup (its query tiles, then its key chunks); the last pool_count
  *     items, from pool_first on, are key chunks that any workgroup takes from a
  *     shared queue once its own list is done.
+ *   tdesc[n_items][8]: per query tile {first query row, tokens, kv head, diagonal
+ *     key of the first token, key end, kv_len, 0, 0}; zero for key chunks.
  *   wgs[grid][8]: per persistent workgroup {first item, query tiles, key chunks,
  *     first block, blocks, chunks run first (0/1), prefill-role tiles, blocks of
  *     those}. Workgroup w runs on die w % 8.

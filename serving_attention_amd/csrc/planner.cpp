@@ -357,7 +357,8 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   const int n_groups = (int)(groups.size() / kGroupWords);
   const int64_t reqs_off = POD_HDR_WORDS;
   const int64_t items_off = reqs_off + (int64_t)reqs.size() * kReqWords;
-  const int64_t wgs_off = items_off + (int64_t)items.size() * kItemWords;
+  const int64_t tdesc_off = items_off + (int64_t)items.size() * kItemWords;
+  const int64_t wgs_off = tdesc_off + (int64_t)items.size() * kTdescWords;
   const int64_t blocks_off = wgs_off + (int64_t)G * kWgWords;
   const int64_t groups_off = blocks_off + n_blocks * kBlockWords;
   const int64_t counters_off = groups_off + (int64_t)n_groups * kGroupWords;
@@ -386,6 +387,7 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   h[15] = (int32_t)(items.size() - pool.size());
   h[16] = (int32_t)pool.size();
   h[17] = (int32_t)queue_off;
+  h[18] = (int32_t)tdesc_off;
   for (size_t i = 0; i < reqs.size(); ++i) {
     int32_t* q = h + reqs_off + i * kReqWords;
     q[0] = reqs[i].qo_start;
@@ -438,6 +440,18 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
         const Item& it = items[i];
         int32_t* dst = h + items_off + k * kItemWords;
         for (int j = 0; j < kItemWords; ++j) dst[j] = it.w[j];
+        // query tiles: what an item boundary needs, without the request table
+        int32_t* td = h + tdesc_off + k * kTdescWords;
+        for (int j = 0; j < kTdescWords; ++j) td[j] = 0;
+        if (!(it.w[0] & kFlagChunk)) {
+          const Req& q = reqs[it.w[1]];
+          td[0] = q.qo_start + it.w[3];
+          td[1] = it.w[4];
+          td[2] = it.w[2];
+          td[3] = q.kv_len - q.qo_len + it.w[3];
+          td[4] = it.w[6];
+          td[5] = q.kv_len;
+        }
         ++k;
         ++((it.w[0] & kFlagRole) ? n_dec : n_pre);
       }
@@ -446,6 +460,7 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
     const Item& it = items[i];
     int32_t* dst = h + items_off + k * kItemWords;
     for (int j = 0; j < kItemWords; ++j) dst[j] = it.w[j];
+    for (int j = 0; j < kTdescWords; ++j) h[tdesc_off + k * kTdescWords + j] = 0;
     ++k;
     ++((it.w[0] & kFlagRole) ? n_dec : n_pre);
   }

@@ -287,6 +287,7 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
   p.items = iws + ctx->hdr[6];
   p.wgs = iws + ctx->hdr[12];
   p.blocks = iws + ctx->hdr[13];
+  p.tdesc = iws + ctx->hdr[18];
   p.groups = iws + ctx->hdr[7];
   p.counters = iws + ctx->hdr[8];
   p.queue = iws + ctx->hdr[17];

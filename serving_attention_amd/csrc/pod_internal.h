@@ -22,6 +22,10 @@ constexpr int kNumXcds = 8;            // MI355X: 8 accelerator dies, 32 CUs eac
 constexpr int kSlotFloats = kChunkRows * kHeadDim + kChunkRows;   // partial O + LSE
 constexpr int kWgWords = 8;            // per-workgroup list header
 constexpr int kBlockWords = 4;         // query-tile block-table entry
+// Per-item boundary data of a query tile, parallel to the items:
+//   {first query row (qo_start + tok0), tokens, kv head, diagonal key of the
+//    first token (kv_len - qo_len + tok0), key end of the item, kv_len, 0, 0}
+constexpr int kTdescWords = 8;
 constexpr int kMaxSinkHeads = 1024;    // sinks staged in LDS by the query tiles
 constexpr int kMaxKvHeads = 16384;     // kv head index fits the block-table entry
 constexpr int kMaxTilesPerWg = 65536;  // tile index fits the block-table entry
@@ -61,6 +65,7 @@ struct Params {
   const int32_t* wgs;       // per workgroup: {first item, tiles, chunks, first block, blocks,
                             //   chunks first, prefill tiles, prefill blocks}
   const int32_t* blocks;    // query-tile block tables
+  const int32_t* tdesc;     // query-tile boundary data, one row per item
   const int32_t* groups;
   int32_t* counters;
   int32_t* queue;           // {next pool item, workgroups done}; zero between launches

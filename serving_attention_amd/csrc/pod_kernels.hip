@@ -354,32 +354,24 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 using CI32x4 = const __attribute__((address_space(4))) i32x4;
 __device__ __forceinline__ CI32* plan_words(const int32_t* p) { return (CI32*)p; }
 
-// one query-tile item, wave-uniform
+// one query-tile item, wave-uniform (its boundary row of the plan: one
+// 32-byte scalar load)
 struct TileDesc {
-  int role, kvh, tok0, ntok, kv_end, qo_start, qo_len, kv_len;
+  int qrow0, ntok, kvh, diag0, kv_end, kv_len;
 };
-__device__ __forceinline__ TileDesc tile_desc(PArg p, CI32* items, int idx) {
-  CI32* it = items + idx * kItemWords;
-  TileDesc d;
-  d.role = it[0] & kFlagRole;
-  d.kvh = it[2];
-  d.tok0 = it[3];
-  d.ntok = it[4];
-  d.kv_end = it[6];
-  CI32* rq = plan_words(p.reqs) + it[1] * kReqWords;
-  d.qo_start = rq[0];
-  d.qo_len = rq[1];
-  d.kv_len = rq[2];
-  return d;
+__device__ __forceinline__ TileDesc tile_desc(CI32* tdesc, int idx) {
+  typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+  const i32x8 w = *reinterpret_cast<const __attribute__((address_space(4))) i32x8*>(tdesc + idx * kTdescWords);
+  return TileDesc{w[0], w[1], w[2], w[3], w[4], w[5]};
 }
 
 
 template <typename T, bool kPow2>
-__device__ void tile_stream(PArg p, int role, const int32_t* titems, const int32_t* tab,
-                            int nv, char* ring, char* idring, float* sink_lds) {
+__device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt, const int32_t* tab,
+                            int nv, char* ring, char* idring, float* sink_lds, char* pf_lds) {
   using V8 = typename Dt<T>::v8;
   CI32* ctab = plan_words(tab);
-  CI32* citems = plan_words(titems);
+  CI32* ctd = plan_words(ttd);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, hi = lane >> 5;
@@ -472,34 +464,62 @@ __device__ void tile_stream(PArg p, int role, const int32_t* titems, const int32
   float m = kNegInf, l = 0.f, sl2 = 0.f;
   RowMask rm;
   // this lane's row of item d: token, qo head; false past the item's rows
-  auto geom = [&](const TileDesc& d, int& tok, int& head) {
+  // the lane's token offset and group head within any tile
+  const int rdiv = row / g, rmod = row % g;
+  // this lane's row of item d: token offset in the tile, qo head; false past
+  // the item's rows
+  auto geom = [&](const TileDesc& d, int& toff, int& head) {
     const bool ok = row < d.ntok * g;
-    tok = d.tok0 + (ok ? row / g : 0);
-    head = d.kvh * g + (ok ? row % g : 0);
+    toff = ok ? rdiv : 0;
+    head = d.kvh * g + (ok ? rmod : 0);
     return ok;
   };
   // item i of the list, and its role, read again where they are needed
   // a use of the query registers: the compiler waits here for the query loads
   // (vmcnt(0), with every load issued before them), so no wait for them is
   // left in the loop.
-  auto query_landed = [&]() {
-    asm volatile("" ::"v"(qreg[0]), "v"(qreg[1]), "v"(qreg[2]), "v"(qreg[3]), "v"(qreg[4]),
-                 "v"(qreg[5]), "v"(qreg[6]), "v"(qreg[7]));
-  };
+  // The next item's query: load c' brings 32 contiguous bytes of each row (16
+  // per lane half: d = 16 c' + 8 hi + [0, 8)), then one swap between the lane
+  // halves per register gives the MFMA layout (lane half hi holds d = 64 hi +
+  // 8 c + [0, 8) in qreg[c]). Using the loaded values makes the compiler wait
+  // for them there (vmcnt(0), with every load issued before them), so no wait
+  // for the query is left in the loop.
+  u32x4 qraw[8];
   auto load_query = [&](int i) {
     PArg q = reload(p);
-    const TileDesc d = tile_desc(q, citems, i);
-    int tok, head;
-    const bool ok = geom(d, tok, head);
-    load_q<T>(qreg, pick_role(q, role, 0), ok, d.qo_start + tok, head, hi);
+    const TileDesc d = tile_desc(ctd, i);
+    int toff, head;
+    const bool ok = geom(d, toff, head);
+    const RoleView r = pick_role(q, role, 0);
+    const T* qp = reinterpret_cast<const T*>(r.q) + (int64_t)(d.qrow0 + toff) * r.q_st +
+                  (int64_t)head * r.q_sh + hi * 8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qraw[c] = ok ? ld16(qp + c * 16) : u32x4{0, 0, 0, 0};
+  };
+  auto query_landed = [&]() {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // lower half keeps qraw[c] and takes the upper half's; the upper half
+        // gets the lower half's qraw[c + 4] and keeps its own
+        const auto sw = __builtin_amdgcn_permlane32_swap(qraw[c][w], qraw[c + 4][w], false, false);
+        qraw[c][w] = sw[0];
+        qraw[c + 4][w] = sw[1];
+      }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      qreg[2 * c] = __builtin_bit_cast(V8, qraw[c]);
+      qreg[2 * c + 1] = __builtin_bit_cast(V8, qraw[c + 4]);
+    }
   };
   auto setup = [&](int i) {
     PArg q = reload(p);
-    const TileDesc d = tile_desc(q, citems, i);
+    const TileDesc d = tile_desc(ctd, i);
     const RoleView r = pick_role(q, role, 0);
-    int tok, head;
-    geom(d, tok, head);
-    const int pdiag = d.kv_len - d.qo_len + tok;
+    int toff, head;
+    geom(d, toff, head);
+    const int pdiag = d.diag0 + toff;
     const int key_hi = min(r.causal ? pdiag : d.kv_len - 1, d.kv_end - 1);
     const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
     rm = row_mask(key_lo, key_hi);
@@ -512,28 +532,48 @@ __device__ void tile_stream(PArg p, int role, const int32_t* titems, const int32
   // normalise (sink folded into the denominator) and store O and the LSE of item d
   auto finish = [&](int i) {
     PArg q = reload(p);
-    const TileDesc d = tile_desc(q, citems, i);
+    const TileDesc d = tile_desc(ctd, i);
     const RoleView r = pick_role(q, role, 0);
-    int tok, head;
-    const bool ok = geom(d, tok, head);
+    int toff, head;
+    const bool ok = geom(d, toff, head);
     const float lt = xhalf_sum(l);
+    const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
+    float den = lt;
+    if (q.sinks) den += fast_exp2(sink_lds[head] * kLog2e - mu2);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    // Output accumulator j = 4a + c of lane half hi is d = db*32 + 8a + 4hi + c.
+    // Per pair a = 2b, 2b+1 one swap between the lane halves (all lanes take
+    // part) leaves each half 8 consecutive d: the lower half d = 16b + [0, 8),
+    // the upper d = 16b + 8 + [0, 8), so each store writes 32 contiguous bytes
+    // of a row.
+    u32x4 ow[4][2];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        typename Dt<T>::v4 pw, qw;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pw[c] = (T)(o[db][8 * b + c] * inv);
+          qw[c] = (T)(o[db][8 * b + 4 + c] * inv);
+        }
+        u32x2 P = __builtin_bit_cast(u32x2, pw), Q = __builtin_bit_cast(u32x2, qw);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(P[w], Q[w], false, false);
+          P[w] = sw[0];
+          Q[w] = sw[1];
+        }
+        ow[db][b] = u32x4{P[0], P[1], Q[0], Q[1]};
+      }
     if (ok) {
-      const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
-      float den = lt;
-      if (q.sinks) den += fast_exp2(sink_lds[head] * kLog2e - mu2);
-      const float inv = den > 0.f ? 1.f / den : 0.f;
-      T* op = reinterpret_cast<T*>(r.out) + (int64_t)(d.qo_start + tok) * r.o_st + (int64_t)head * r.o_sh;
+      T* op = reinterpret_cast<T*>(r.out) + (int64_t)(d.qrow0 + toff) * r.o_st + (int64_t)head * r.o_sh + hi * 8;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          typename Dt<T>::v4 w;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) w[c] = (T)(o[db][4 * a + c] * inv);
-          *reinterpret_cast<u32x2*>(op + db * 32 + acc_d(4 * a, hi)) = __builtin_bit_cast(u32x2, w);
-        }
+        for (int b = 0; b < 2; ++b) *reinterpret_cast<u32x4*>(op + db * 32 + 16 * b) = ow[db][b];
       if (r.lse && hi == 0)
-        r.lse[(int64_t)(d.qo_start + tok) * q.num_qo_heads + head] = lt > 0.f ? mu2 + fast_log2(lt) : kNegInf;
+        r.lse[(int64_t)(d.qrow0 + toff) * q.num_qo_heads + head] = lt > 0.f ? mu2 + fast_log2(lt) : kNegInf;
     }
   };
 
@@ -622,6 +662,17 @@ __device__ void tile_stream(PArg p, int role, const int32_t* titems, const int32
   // copy, for the tiles' final normalisation) and the first tile's query.
   setup(cur);
   load_query(cur);
+  // Pull the block table and the tiles' boundary rows into L2 (one word per
+  // 64-byte line, up to 16 KB each), so the scalar loads of them hit there;
+  // the words land in a scratch LDS area nobody reads.
+  {
+    const int lines = min((nv * kBlockWords * 4 + 63) / 64, 256);
+    for (int c = wave; c * 64 < lines; c += kWaves)
+      lds_dma4(tab + min(c * 64 + lane, lines - 1) * 16, pf_lds);
+    const int tlines = min((nt * kTdescWords * 4 + 63) / 64, 256);
+    for (int c = wave; c * 64 < tlines; c += kWaves)
+      lds_dma4(ttd + t0 * kTdescWords + min(c * 64 + lane, tlines - 1) * 16, pf_lds);
+  }
   if (p.sinks) {
     for (int c = wave; c * 64 < p.num_qo_heads; c += kWaves)
       lds_dma4(p.sinks + min(c * 64 + lane, p.num_qo_heads - 1), (char*)sink_lds + c * 256);
@@ -1048,6 +1099,8 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
   // sink logits for the query tiles' normalisation
   __shared__ __attribute__((aligned(16))) float sink_lds[kMaxSinkHeads];
   __shared__ int pool_slot;
+  // destination of the block-table prefetch
+  __shared__ __attribute__((aligned(16))) char pf_lds[256];
   CI32* wg = plan_words(p.wgs) + blockIdx.x * kWgWords;
   const int first_item = wg[0], n_tiles = wg[1], n_chunks = wg[2];
   const int first_blk = wg[3], n_blk = wg[4];
@@ -1070,7 +1123,8 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
   if (chunks_first) run_chunks();
   if (n_tiles > 0) {
     __syncthreads();
-    const int32_t* ti = p.items + (int64_t)first_item * kItemWords;
+    const int32_t* ttd = p.tdesc + (int64_t)first_item * kTdescWords;
+    const int pre_tiles = wg[6];
     const int32_t* tb = p.blocks + (int64_t)first_blk * kBlockWords;
     // one block stream per role: the prefill tiles, then the decode tiles
     const int pre_blk = wg[7];
@@ -1078,10 +1132,11 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
       const int b0 = role ? pre_blk : 0, nb = role ? n_blk - pre_blk : pre_blk;
       if (nb == 0) continue;
       if (role && pre_blk) __syncthreads();
+      const int t0 = role ? pre_tiles : 0, nt = role ? n_tiles - pre_tiles : pre_tiles;
       if (p.page_shift >= 0)
-        tile_stream<T, true>(p, role, ti, tb + (int64_t)b0 * kBlockWords, nb, lds, ids, sink_lds);
+        tile_stream<T, true>(p, role, ttd, t0, nt, tb + (int64_t)b0 * kBlockWords, nb, lds, ids, sink_lds, pf_lds);
       else
-        tile_stream<T, false>(p, role, ti, tb + (int64_t)b0 * kBlockWords, nb, lds, ids, sink_lds);
+        tile_stream<T, false>(p, role, ttd, t0, nt, tb + (int64_t)b0 * kBlockWords, nb, lds, ids, sink_lds, pf_lds);
     }
   }
   if (!chunks_first) run_chunks();

@@ -61,7 +61,8 @@ def decode_image(img):
         wg_of_item[first:first + nt + nc] = w
     pool_first, pool_count = int(h[15]), int(h[16])
     queue = img[h[17]:h[17] + 2]
+    tdesc = img[h[18]:h[18] + 8 * n_items].reshape(n_items, 8)
     return dict(n_items=n_items, grid=grid, reqs=reqs, items=items, wgs=wgs, blocks=blocks,
                 wg_of_item=wg_of_item, groups=groups, counters=counters, n_slots=int(h[9]),
                 slot_floats=int(h[10]), chunk=int(h[11]), pool_first=pool_first,
-                pool_count=pool_count, queue=queue)
+                pool_count=pool_count, queue=queue, tdesc=tdesc)

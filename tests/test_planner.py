@@ -262,6 +262,15 @@ def test_block_tables(wl):
         assert npb == n_pre_blocks
         total += nb
     assert total == len(blocks)
+    # each query tile's boundary row: first query row, tokens, kv head, diagonal
+    # key of its first token, key end, kv_len; zero rows for key chunks
+    for it, td in zip(items, im["tdesc"]):
+        if int(it[0]) & FLAG_CHUNK:
+            assert not td.any()
+            continue
+        qs, ql, kl = (int(x) for x in reqs[int(it[1])][:3])
+        assert [int(x) for x in td] == [qs + int(it[3]), int(it[4]), int(it[2]),
+                                        kl - ql + int(it[3]), int(it[6]), kl, 0, 0]
 
 
 def test_workspace_sizes():
