@@ -289,12 +289,15 @@ __device__ __forceinline__ RowMask row_mask(int key_lo, int key_hi) {
 template <int NB>
 __device__ __forceinline__ void update_max(f32x16 (&s)[NB], float sl2, float& m, float& l,
                                            f32x16 (&o)[4]) {
-  float mx = kNegInf;
+  float mx0 = kNegInf, mx1 = kNegInf;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
-    for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[b][j]);
-  mx = xhalf_max(mx);
+    for (int j = 0; j < 16; j += 2) {
+      mx0 = fmaxf(mx0, s[b][j]);
+      mx1 = fmaxf(mx1, s[b][j + 1]);
+    }
+  float mx = xhalf_max(fmaxf(mx0, mx1));
   const bool upd = (m == kNegInf) ? (mx != kNegInf) : ((mx - m) * sl2 > kRescaleThreshold);
   if (__any(upd)) {
     const float mn = upd ? mx : m;
@@ -649,8 +652,18 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
     }
     update_max<2>(s, sl2, m, l, o);
     const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
+    float la[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) exp_block<T>(s[h], sl2, mu2, l, pb[h]);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float e = fast_exp2(fmaf(s[h][8 * hh + i], sl2, -mu2));
+          la[i & 3] += e;
+          pb[h][hh][i] = (T)e;
+        }
+    l += (la[0] + la[1]) + (la[2] + la[3]);
     __builtin_amdgcn_s_setprio(0);
   };
 
