@@ -170,7 +170,7 @@ typedef struct pod_plan_info {
   int32_t decode_chunk;     /* keys per decode split actually used */
   int32_t image_ints;       /* int32 words of the work-list image */
   int64_t float_ws_bytes;   /* float workspace the plan needs */
-  int64_t int_ws_bytes;     /* int workspace the plan needs */
+  int64_t int_ws_bytes;     /* int workspace the plan needs (two image halves) */
 } pod_plan_info;
 
 typedef struct pod_ctx* pod_ctx_t;
@@ -188,10 +188,14 @@ int pod_create(pod_ctx_t* out, int device, void* float_ws, size_t float_ws_bytes
 int pod_destroy(pod_ctx_t ctx);
 
 /*
- * Validate `desc`, build the work list on the host and enqueue its copy into the
- * int workspace on `stream` (a hipStream_t; NULL = default stream). The copy is
- * stream-ordered, so a pod_run() on the same stream sees it. Not to be called
- * during stream capture. Replaces any previous plan of this context.
+ * Validate `desc`, build the work list on the host and start its copy to the
+ * device. Plans alternate between the two halves of the int workspace; the copy
+ * runs on a stream the context owns, once the launches of the plan before last
+ * (which read the same half) have finished (the host waits for that if needed),
+ * so it overlaps the previous plan's launches. The next pod_run() waits for the copy (on its own stream), so no
+ * further ordering is needed. `stream` is unused (kept for symmetry with
+ * pod_run). Not to be called during stream capture. Replaces any previous plan
+ * of this context.
  */
 int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream);
 
@@ -199,10 +203,11 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream);
 int pod_plan_stats(pod_ctx_t ctx, pod_plan_info* info);
 
 /*
- * Enqueue the fused attention launch on `stream`: exactly one kernel launch
- * (none if the plan holds no work). Buffers must match the plan's shapes and
- * dtype. Asynchronous; allocates nothing; leaves the workspace counters at zero
- * when the launch completes, so runs can be repeated without a re-plan.
+ * Enqueue the fused attention launch on `stream`: a wait for the current plan's
+ * work-list copy, then exactly one kernel launch (none if the plan holds no
+ * work). Buffers must match the plan's shapes and dtype. Asynchronous;
+ * allocates nothing; leaves the workspace counters at zero when the launch
+ * completes, so runs can be repeated without a re-plan.
  */
 int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream);
 

@@ -105,7 +105,7 @@ int validate_role(const pod_role_desc& r, const char* name, int page_size, std::
 
 }  // namespace
 
-int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_info& info,
+int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& info,
                  std::string* err) {
   info = pod_plan_info{};
   if (d.num_qo_heads <= 0 || d.num_kv_heads <= 0)
@@ -329,30 +329,45 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   // Workgroups: one persistent workgroup per CU; workgroup w is dispatched to
   // die w % kNumXcds. Each die's items, heaviest first, go to the least loaded
   // of its workgroups (LPT), so every workgroup holds a static list.
-  std::vector<std::vector<uint32_t>> wg_tiles(G), wg_chunks(G);
-  std::vector<int64_t> wg_load(G, 0);
-  for (uint32_t i : order) {
-    if (in_pool[i]) continue;
-    const Item& it = items[i];
-    int best = -1;
-    for (int w = it.xcd; w < G; w += kNumXcds)
-      if (best < 0 || wg_load[w] < wg_load[best]) best = w;
-    if (best < 0) best = (int)(i % (uint32_t)G);   // fewer workgroups than dies
-    wg_load[best] += it.cost;
-    ((it.w[0] & kFlagChunk) ? wg_chunks : wg_tiles)[best].push_back(i);
+  // Per die a min-heap of (load, workgroup); ties go to the lower workgroup.
+  std::vector<int32_t> wg_of(items.size(), -1);
+  {
+    using Slot = std::pair<int64_t, int32_t>;
+    std::vector<Slot> heap[kNumXcds];
+    for (int w = 0; w < G; ++w) heap[w % kNumXcds].push_back(Slot(0, w));
+    auto later = [](const Slot& a, const Slot& b) { return a > b; };
+    for (uint32_t i : order) {
+      if (in_pool[i]) continue;
+      std::vector<Slot>& hp = heap[items[i].xcd < G ? items[i].xcd : items[i].xcd % G];
+      std::pop_heap(hp.begin(), hp.end(), later);
+      wg_of[i] = hp.back().second;
+      hp.back().first += items[i].cost;
+      std::push_heap(hp.begin(), hp.end(), later);
+    }
   }
-  // a workgroup's query tiles run as one block stream per role: prefill first
-  for (int w = 0; w < G; ++w)
-    std::stable_partition(wg_tiles[w].begin(), wg_tiles[w].end(),
-                          [&](uint32_t i) { return (items[i].w[0] & kFlagRole) == 0; });
+  // Each workgroup's list, heaviest first within each kind: prefill-role query
+  // tiles, decode-role query tiles (a workgroup runs one block stream per
+  // role), then key chunks. One stable counting sort on (workgroup, kind).
+  auto kind = [&](const Item& it) { return (it.w[0] & kFlagChunk) ? 2 : (it.w[0] & kFlagRole); };
+  std::vector<int32_t> bucket((size_t)G * 3 + 1, 0);
+  for (uint32_t i : order)
+    if (wg_of[i] >= 0) ++bucket[(size_t)wg_of[i] * 3 + kind(items[i]) + 1];
+  for (size_t b = 0; b + 1 < bucket.size(); ++b) bucket[b + 1] += bucket[b];
+  std::vector<uint32_t> listed(bucket.back());
+  {
+    std::vector<int32_t> fill(bucket.begin(), bucket.end() - 1);
+    for (uint32_t i : order)
+      if (wg_of[i] >= 0) listed[fill[(size_t)wg_of[i] * 3 + kind(items[i])]++] = i;
+  }
 
   // query-tile blocks per workgroup
   int64_t n_blocks = 0;
   for (int w = 0; w < G; ++w) {
-    if (wg_tiles[w].size() >= (size_t)kMaxTilesPerWg)
+    if (bucket[(size_t)w * 3 + 2] - bucket[(size_t)w * 3] >= kMaxTilesPerWg)
       return fail(err, POD_ERR_UNSUPPORTED, "plan too large (query tiles per workgroup)");
-    for (uint32_t i : wg_tiles[w]) n_blocks += (items[i].w[6] - items[i].w[5] + kTileKeys - 1) / kTileKeys;
   }
+  for (uint32_t i : listed)
+    if (!(items[i].w[0] & kFlagChunk)) n_blocks += (items[i].w[6] - items[i].w[5] + kTileKeys - 1) / kTileKeys;
 
   const int n_groups = (int)(groups.size() / kGroupWords);
   const int64_t reqs_off = POD_HDR_WORDS;
@@ -366,8 +381,20 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   const int64_t total = queue_off + 2;
   if (total > INT32_MAX / 2) return fail(err, POD_ERR_UNSUPPORTED, "plan too large");
 
-  image.resize((size_t)total);
-  int32_t* h = image.data();
+  info.n_items = (int32_t)items.size();
+  info.n_prefill_items = 0;
+  for (const Item& it : items) info.n_prefill_items += (it.w[0] & kFlagRole) == 0;
+  info.n_decode_items = info.n_items - info.n_prefill_items;
+  info.n_groups = n_groups;
+  info.n_slots = n_slots;
+  info.grid = G;
+  info.decode_chunk = (int32_t)std::min<int64_t>(C, INT32_MAX);
+  info.image_ints = (int32_t)total;
+  info.float_ws_bytes = (int64_t)n_slots * kSlotFloats * 4;
+  // two plans alternate between the halves of the int workspace
+  info.int_ws_bytes = 2 * ((total * 4 + 255) / 256 * 256);
+  int32_t* h = sink ? sink((size_t)total) : nullptr;
+  if (!h) return POD_OK;   // sizes only
   std::fill(h, h + POD_HDR_WORDS, 0);
   h[0] = POD_IMAGE_MAGIC;
   h[1] = (int32_t)items.size();
@@ -398,23 +425,25 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   int n_pre = 0, n_dec = 0;
   int64_t k = 0, blk = 0;
   for (int w = 0; w < G; ++w) {
-    const std::vector<uint32_t>& tl = wg_tiles[w];
-    const std::vector<uint32_t>& cl = wg_chunks[w];
+    const uint32_t* tl = listed.data() + bucket[(size_t)w * 3];
+    const size_t nt = (size_t)(bucket[(size_t)w * 3 + 2] - bucket[(size_t)w * 3]);
+    const uint32_t* cl = tl + nt;
+    const size_t nc = (size_t)(bucket[(size_t)w * 3 + 3] - bucket[(size_t)w * 3 + 2]);
     int32_t* wg = h + wgs_off + (int64_t)w * kWgWords;
     bool chunks_first;
-    if (tl.empty() || cl.empty()) chunks_first = false;
+    if (nt == 0 || nc == 0) chunks_first = false;
     else if (d.order == POD_ORDER_PREFILL_FIRST) chunks_first = false;
     else if (d.order == POD_ORDER_DECODE_FIRST) chunks_first = true;
     else if (d.order == POD_ORDER_LONGEST_FIRST) chunks_first = items[cl[0]].cost > items[tl[0]].cost;
     else chunks_first = ((w / kNumXcds) & 1) != 0;   // half of each die's workgroups each way
     wg[0] = (int32_t)k;
-    wg[1] = (int32_t)tl.size();
-    wg[2] = (int32_t)cl.size();
+    wg[1] = (int32_t)nt;
+    wg[2] = (int32_t)nc;
     wg[3] = (int32_t)blk;
     wg[5] = chunks_first ? 1 : 0;
     int64_t nb = 0;
     int32_t n_pre_tiles = 0, n_pre_blocks = 0;
-    for (size_t j = 0; j < tl.size(); ++j) {
+    for (size_t j = 0; j < nt; ++j) {
       const Item& it = items[tl[j]];
       if ((it.w[0] & kFlagRole) == 0) {
         ++n_pre_tiles;
@@ -435,26 +464,25 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
     wg[6] = n_pre_tiles;
     wg[7] = n_pre_blocks;
     blk += nb;
-    for (const std::vector<uint32_t>* lst : {&tl, &cl})
-      for (uint32_t i : *lst) {
-        const Item& it = items[i];
-        int32_t* dst = h + items_off + k * kItemWords;
-        for (int j = 0; j < kItemWords; ++j) dst[j] = it.w[j];
-        // query tiles: what an item boundary needs, without the request table
-        int32_t* td = h + tdesc_off + k * kTdescWords;
-        for (int j = 0; j < kTdescWords; ++j) td[j] = 0;
-        if (!(it.w[0] & kFlagChunk)) {
-          const Req& q = reqs[it.w[1]];
-          td[0] = q.qo_start + it.w[3];
-          td[1] = it.w[4];
-          td[2] = it.w[2];
-          td[3] = q.kv_len - q.qo_len + it.w[3];
-          td[4] = it.w[6];
-          td[5] = q.kv_len;
-        }
-        ++k;
-        ++((it.w[0] & kFlagRole) ? n_dec : n_pre);
+    for (size_t j = 0; j < nt + nc; ++j) {
+      const Item& it = items[tl[j]];
+      int32_t* dst = h + items_off + k * kItemWords;
+      for (int x = 0; x < kItemWords; ++x) dst[x] = it.w[x];
+      // query tiles: what an item boundary needs, without the request table
+      int32_t* td = h + tdesc_off + k * kTdescWords;
+      for (int x = 0; x < kTdescWords; ++x) td[x] = 0;
+      if (!(it.w[0] & kFlagChunk)) {
+        const Req& q = reqs[it.w[1]];
+        td[0] = q.qo_start + it.w[3];
+        td[1] = it.w[4];
+        td[2] = it.w[2];
+        td[3] = q.kv_len - q.qo_len + it.w[3];
+        td[4] = it.w[6];
+        td[5] = q.kv_len;
       }
+      ++k;
+      ++((it.w[0] & kFlagRole) ? n_dec : n_pre);
+    }
   }
   for (uint32_t i : pool) {
     const Item& it = items[i];
@@ -469,16 +497,8 @@ int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_i
   h[queue_off] = 0;
   h[queue_off + 1] = 0;
 
-  info.n_items = (int32_t)items.size();
-  info.n_prefill_items = n_pre;
-  info.n_decode_items = n_dec;
-  info.n_groups = n_groups;
-  info.n_slots = n_slots;
-  info.grid = G;
-  info.decode_chunk = (int32_t)std::min<int64_t>(C, INT32_MAX);
-  info.image_ints = (int32_t)total;
-  info.float_ws_bytes = (int64_t)n_slots * kSlotFloats * 4;
-  info.int_ws_bytes = total * 4;
+  (void)n_pre;
+  (void)n_dec;
   return POD_OK;
 }
 

@@ -11,11 +11,6 @@
 
 #include "pod_internal.h"
 
-namespace pod {
-int plan_compute(const pod_plan_desc& d, std::vector<int32_t>& image, pod_plan_info& info,
-                 std::string* err);
-}
-
 namespace {
 
 thread_local std::string g_err;
@@ -52,15 +47,27 @@ struct pod_ctx {
   int32_t num_qo_heads = 0, num_kv_heads = 0, page_size = 0, dtype = 0, has_sinks = 0;
   pod_plan_info info{};
   int32_t hdr[POD_HDR_WORDS] = {};
-  // two pinned staging buffers, reused once their last copy has completed
+  // Plans alternate between two halves of the int workspace, each with a
+  // pinned staging buffer; the image goes up on a library stream while the
+  // previous plan's kernels may still run, and pod_run waits for it.
   int32_t* staging[2] = {nullptr, nullptr};
   size_t staging_cap[2] = {0, 0};
-  hipEvent_t staged[2] = {nullptr, nullptr};
+  hipEvent_t staged[2] = {nullptr, nullptr};   // copy of plan k done (host and device side)
   bool staged_pending[2] = {false, false};
+  hipEvent_t used[2] = {nullptr, nullptr};     // last launch that read half k done
+  bool used_pending[2] = {false, false};
+  hipStream_t copy_stream = nullptr;
   int next_staging = 0;
+  int cur = 0;                                 // half of the current plan
 };
 
 namespace {
+
+// half k of the int workspace (256-byte aligned; each half holds one plan)
+int32_t* int_half(const pod_ctx* c, int k) {
+  const size_t half = (c->int_bytes / 2) & ~(size_t)255;
+  return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(c->int_ws) + (size_t)k * half);
+}
 
 struct DeviceGuard {
   int prev = -1;
@@ -84,25 +91,25 @@ const char* pod_last_error(void) { return g_err.c_str(); }
 int pod_plan_compute(const pod_plan_desc* desc, int32_t* image, size_t image_cap,
                      pod_plan_info* info) {
   if (!desc) return set_err(POD_ERR_INVALID, "desc is NULL");
-  std::vector<int32_t> img;
   pod_plan_info inf;
   std::string err;
-  int rc = pod::plan_compute(*desc, img, inf, &err);
+  bool fits = true;
+  int rc = pod::plan_compute(*desc, [&](size_t n) -> int32_t* {
+    fits = image != nullptr && n <= image_cap;
+    return fits ? image : nullptr;
+  }, inf, &err);
   if (rc) return set_err(rc, err);
   if (info) *info = inf;
-  if (img.size() > image_cap || (!image && !img.empty()))
-    return set_err(POD_ERR_WORKSPACE, "image buffer too small for the plan");
-  if (!img.empty()) memcpy(image, img.data(), img.size() * sizeof(int32_t));
+  if (!fits) return set_err(POD_ERR_WORKSPACE, "image buffer too small for the plan");
   g_err.clear();
   return POD_OK;
 }
 
 int pod_workspace_bytes(const pod_plan_desc* desc, size_t* float_ws_bytes, size_t* int_ws_bytes) {
   if (!desc) return set_err(POD_ERR_INVALID, "desc is NULL");
-  std::vector<int32_t> img;
   pod_plan_info inf;
   std::string err;
-  int rc = pod::plan_compute(*desc, img, inf, &err);
+  int rc = pod::plan_compute(*desc, nullptr, inf, &err);
   if (rc) return set_err(rc, err);
   if (float_ws_bytes) *float_ws_bytes = (size_t)inf.float_ws_bytes;
   if (int_ws_bytes) *int_ws_bytes = (size_t)inf.int_ws_bytes;
@@ -146,8 +153,13 @@ int pod_destroy(pod_ctx_t ctx) {
         (void)hipEventSynchronize(ctx->staged[i]);
         (void)hipEventDestroy(ctx->staged[i]);
       }
+      if (ctx->used[i]) {
+        (void)hipEventSynchronize(ctx->used[i]);
+        (void)hipEventDestroy(ctx->used[i]);
+      }
       if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
     }
+    if (ctx->copy_stream) (void)hipStreamDestroy(ctx->copy_stream);
   }
   delete ctx;
   return POD_OK;
@@ -158,47 +170,70 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   if (!desc) return set_err(POD_ERR_INVALID, "desc is NULL");
   pod_plan_desc d = *desc;
   if (d.num_cus <= 0) d.num_cus = ctx->num_cus;
-  std::vector<int32_t> img;
+  DeviceGuard dg(ctx->device);
+  if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
+  (void)stream;   // the copy runs on the library's stream; pod_run waits for it
+  // The planner writes the image straight into a pinned staging buffer (two
+  // alternate, each reused once its previous copy has completed).
+  const int k = ctx->next_staging;
+  hipError_t e = hipSuccess;
+  const char* what = nullptr;
+  size_t bytes = 0;
+  auto sink = [&](size_t n) -> int32_t* {
+    bytes = n * sizeof(int32_t);
+    if (ctx->staged_pending[k]) {
+      e = hipEventSynchronize(ctx->staged[k]);
+      if (e != hipSuccess) { what = "hipEventSynchronize"; return nullptr; }
+      ctx->staged_pending[k] = false;
+    }
+    if (ctx->staging_cap[k] < bytes) {
+      if (ctx->staging[k]) (void)hipHostFree(ctx->staging[k]);
+      ctx->staging[k] = nullptr;
+      ctx->staging_cap[k] = 0;
+      size_t cap = bytes < 65536 ? 65536 : bytes * 2;
+      e = hipHostMalloc(reinterpret_cast<void**>(&ctx->staging[k]), cap, hipHostMallocDefault);
+      if (e != hipSuccess) { what = "hipHostMalloc"; return nullptr; }
+      ctx->staging_cap[k] = cap;
+    }
+    return ctx->staging[k];
+  };
   pod_plan_info inf;
   std::string err;
-  int rc = pod::plan_compute(d, img, inf, &err);
+  int rc = pod::plan_compute(d, sink, inf, &err);
   if (rc) return set_err(rc, err);
+  if (what) return hip_err(e, what);
   if ((size_t)inf.int_ws_bytes > ctx->int_bytes)
     return set_err(POD_ERR_WORKSPACE, "int workspace too small: need " +
                                           std::to_string(inf.int_ws_bytes) + " bytes");
+  if (!ctx->copy_stream) {
+    e = hipStreamCreateWithFlags(&ctx->copy_stream, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_err(e, "hipStreamCreate");
+  }
   if ((size_t)inf.float_ws_bytes > ctx->float_bytes)
     return set_err(POD_ERR_WORKSPACE, "float workspace too small: need " +
                                           std::to_string(inf.float_ws_bytes) + " bytes");
-  DeviceGuard dg(ctx->device);
-  if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int k = ctx->next_staging;
-  hipError_t e;
-  if (ctx->staged_pending[k]) {
-    e = hipEventSynchronize(ctx->staged[k]);
-    if (e != hipSuccess) return hip_err(e, "hipEventSynchronize");
-    ctx->staged_pending[k] = false;
-  }
-  const size_t bytes = img.size() * sizeof(int32_t);
-  if (ctx->staging_cap[k] < bytes) {
-    if (ctx->staging[k]) (void)hipHostFree(ctx->staging[k]);
-    ctx->staging[k] = nullptr;
-    ctx->staging_cap[k] = 0;
-    size_t cap = bytes < 65536 ? 65536 : bytes * 2;
-    e = hipHostMalloc(reinterpret_cast<void**>(&ctx->staging[k]), cap, hipHostMallocDefault);
-    if (e != hipSuccess) return hip_err(e, "hipHostMalloc");
-    ctx->staging_cap[k] = cap;
-  }
   if (!ctx->staged[k]) {
     e = hipEventCreateWithFlags(&ctx->staged[k], hipEventDisableTiming);
     if (e != hipSuccess) return hip_err(e, "hipEventCreate");
   }
-  memcpy(ctx->staging[k], img.data(), bytes);
-  e = hipMemcpyAsync(ctx->int_ws, ctx->staging[k], bytes, hipMemcpyHostToDevice, s);
+  if (!ctx->used[k]) {   // a launch's stop event (hipExtLaunchKernel)
+    e = hipEventCreate(&ctx->used[k]);
+    if (e != hipSuccess) return hip_err(e, "hipEventCreate");
+  }
+  // half k is free once the launches that read it (the plan before last) are
+  // done; the host checks that (they normally are), so the copy stream carries
+  // no wait on the launch stream
+  if (ctx->used_pending[k]) {
+    e = hipEventSynchronize(ctx->used[k]);
+    if (e != hipSuccess) return hip_err(e, "hipEventSynchronize");
+    ctx->used_pending[k] = false;
+  }
+  e = hipMemcpyAsync(int_half(ctx, k), ctx->staging[k], bytes, hipMemcpyHostToDevice, ctx->copy_stream);
   if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (work list)");
-  e = hipEventRecord(ctx->staged[k], s);
+  e = hipEventRecord(ctx->staged[k], ctx->copy_stream);
   if (e != hipSuccess) return hip_err(e, "hipEventRecord");
   ctx->staged_pending[k] = true;
+  ctx->cur = k;
   ctx->next_staging = 1 - k;
 
   const pod_role_desc* rd[2] = {&d.prefill, &d.decode};
@@ -216,7 +251,7 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   ctx->dtype = d.dtype;
   ctx->has_sinks = d.has_sinks ? 1 : 0;
   ctx->info = inf;
-  memcpy(ctx->hdr, img.data(), sizeof(ctx->hdr));
+  memcpy(ctx->hdr, ctx->staging[k], sizeof(ctx->hdr));
   ctx->planned = true;
   g_err.clear();
   return POD_OK;
@@ -282,7 +317,7 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     o.causal = rp.causal;
     o.window_left = rp.window_left;
   }
-  int32_t* iws = reinterpret_cast<int32_t*>(ctx->int_ws);
+  int32_t* iws = int_half(ctx, ctx->cur);
   p.reqs = iws + ctx->hdr[5];
   p.items = iws + ctx->hdr[6];
   p.wgs = iws + ctx->hdr[12];
@@ -304,8 +339,25 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     if ((1 << sh) == ctx->page_size) p.page_shift = sh;
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
-  int e = pod::launch_pod_grid(p, ctx->dtype, ctx->info.grid, stream);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // this plan's work list must be up; a stream wait only while its copy runs
+  hipError_t he = hipSuccess;
+  if (ctx->staged_pending[ctx->cur]) {
+    he = hipEventQuery(ctx->staged[ctx->cur]);
+    if (he == hipSuccess) {
+      ctx->staged_pending[ctx->cur] = false;
+    } else if (he == hipErrorNotReady) {
+      he = hipStreamWaitEvent(s, ctx->staged[ctx->cur], 0);
+      if (he != hipSuccess) return hip_err(he, "hipStreamWaitEvent");
+    } else {
+      return hip_err(he, "hipEventQuery");
+    }
+  }
+  // used[cur] fires when this launch completes (a launch that is not issued
+  // because the plan holds no work reads nothing)
+  int e = pod::launch_pod_grid(p, ctx->dtype, ctx->info.grid, stream, ctx->used[ctx->cur]);
   if (e != (int)hipSuccess) return hip_err((hipError_t)e, "pod grid launch");
+  if (ctx->info.grid > 0) ctx->used_pending[ctx->cur] = true;
   g_err.clear();
   return POD_OK;
 }

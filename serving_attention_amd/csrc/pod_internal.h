@@ -5,6 +5,9 @@
 
 #include <stdint.h>
 
+#include <functional>
+#include <string>
+
 #include "pod_attn.h"
 
 namespace pod {
@@ -80,7 +83,15 @@ struct Params {
   int32_t page_shift;       // log2(page_size) when it is a power of two, else -1
 };
 
-// Launch the fused grid on `stream` (a hipStream_t). Returns a hipError_t value.
-int launch_pod_grid(const Params& p, int dtype, int grid, void* stream);
+// Host planner (planner.cpp). It validates `d`, fills `info`, and asks `sink`
+// for a buffer of info.image_ints words to write the work-list image into; a
+// null sink, or a sink that returns nullptr, computes the sizes only.
+using ImageSink = std::function<int32_t*(size_t)>;
+int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& info,
+                 std::string* err);
+
+// Launch the fused grid on `stream` (a hipStream_t); `done_event` (a hipEvent_t,
+// or null) is signalled when the launch completes. Returns a hipError_t value.
+int launch_pod_grid(const Params& p, int dtype, int grid, void* stream, void* done_event);
 
 }  // namespace pod

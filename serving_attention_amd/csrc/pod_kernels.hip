@@ -31,6 +31,7 @@
 // 4-key x 16-dim blocks read by ds_read_b64_tr_b16 for the V^T operand fall in
 // disjoint banks for the two 16-lane groups of each half wave.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <math.h>
 
@@ -1173,13 +1174,15 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
 
 }  // namespace
 
-int launch_pod_grid(const Params& p, int dtype, int grid, void* stream) {
+int launch_pod_grid(const Params& p, int dtype, int grid, void* stream, void* done_event) {
   if (grid <= 0) return (int)hipSuccess;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t done = reinterpret_cast<hipEvent_t>(done_event);
+  // the completion event rides on the dispatch itself (no separate marker)
   if (dtype == POD_DTYPE_BF16)
-    hipLaunchKernelGGL(pod_grid_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, s, p);
+    hipExtLaunchKernelGGL(pod_grid_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, s, nullptr, done, 0, p);
   else
-    hipLaunchKernelGGL(pod_grid_kernel<_Float16>, dim3(grid), dim3(kThreads), 0, s, p);
+    hipExtLaunchKernelGGL(pod_grid_kernel<_Float16>, dim3(grid), dim3(kThreads), 0, s, nullptr, done, 0, p);
   return (int)hipGetLastError();
 }
 
