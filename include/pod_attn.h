@@ -74,7 +74,8 @@ enum {
  *   window_left   -1 = off; else row i also drops keys before p_i - window_left,
  *                 p_i = kv_len - q_len + i, so window_left keys strictly before the
  *                 diagonal plus the diagonal remain ([CUDNN] window alignment note).
- *   sm_scale      softmax scale; <= 0 selects 1/sqrt(head_dim) ([POD] "Prefill 侧参数").
+ *   sm_scale      softmax scale; <= 0 selects 1/sqrt(head_dim) ([POD] "Prefill 侧参数");
+ *                 above 1e6 (or NaN) is refused with POD_ERR_INVALID.
  */
 typedef struct pod_role_desc {
   int32_t batch;

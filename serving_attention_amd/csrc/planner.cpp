@@ -60,6 +60,12 @@ int validate_role(const pod_role_desc& r, const char* name, int page_size, std::
     return fail(err, POD_ERR_INVALID, buf);
   }
   if (r.batch == 0) return POD_OK;
+  // the kernels keep scores times scale_log2 in fp32 next to a -1e30 start
+  // value; scales beyond 1e6 (or NaN) are refused
+  if (!(r.sm_scale <= 1e6f)) {
+    snprintf(buf, sizeof buf, "%s.sm_scale must be <= 1e6", name);
+    return fail(err, POD_ERR_INVALID, buf);
+  }
   if (!r.qo_indptr || !r.kv_indptr || !r.last_page_len) {
     snprintf(buf, sizeof buf, "%s: qo_indptr, kv_indptr and last_page_len are required", name);
     return fail(err, POD_ERR_INVALID, buf);

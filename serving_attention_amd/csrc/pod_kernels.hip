@@ -98,9 +98,29 @@ constexpr int kLdsMain = kMax2(kMax2(kRingSlots * kTileBuf, kWaves * kWaveLds), 
 static_assert(kLdsMain + kRingSlots * kIdSlot <= 160 * 1024, "LDS budget");
 // the running max moves only when a block's max exceeds it by this much (log2 units)
 constexpr float kRescaleThreshold = 8.f;
+// Start of a query-tile row's running max (raw score units): finite, so the
+// bound test and the exponent need no case for a row that has seen no valid
+// key yet. The max is only a reference point (P = exp2(sl2 (s - m)) for any m
+// that keeps sl2 (s - m) below the threshold): the first block with a valid key
+// usually moves it, scaling the still-zero state by exp2(-huge) = 0, and while
+// no key is valid every exponent is -inf.
+constexpr float kMaxInit = -1e30f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Maximum of two or three scores with one instruction and no NaN quieting
+// (scores are finite or -inf; fmaxf adds a canonicalising max per operand).
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 
 // Value from the other lane half (lane ^ 32) combined with the own value.
 __device__ __forceinline__ float xhalf_max(float v) {
@@ -465,7 +485,8 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
   int cur = item_idx(ea);
   V8 qreg[8];
   f32x16 o[4];
-  float m = kNegInf, l = 0.f, sl2 = 0.f;
+  // running max (raw units) and row sum (this lane half's keys)
+  float m = kMaxInit, l = 0.f, sl2 = 0.f;
   RowMask rm;
   // this lane's row of item d: token, qo head; false past the item's rows
   // the lane's token offset and group head within any tile
@@ -528,7 +549,7 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
     const int key_lo = r.window_left >= 0 ? max(0, pdiag - r.window_left) : 0;
     rm = row_mask(key_lo, key_hi);
     sl2 = r.scale_log2;
-    m = kNegInf;
+    m = kMaxInit;
     l = 0.f;
 #pragma unroll
     for (int b = 0; b < 4; ++b) o[b] = f32x16{};
@@ -541,7 +562,9 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
     int toff, head;
     const bool ok = geom(d, toff, head);
     const float lt = xhalf_sum(l);
-    const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
+    // log2 offset of the row's values (if no key was valid, l is 0 and a sink
+    // term comes out +inf, so O = 0)
+    const float mu2 = m * sl2;
     float den = lt;
     if (q.sinks) den += fast_exp2(sink_lds[head] * kLog2e - mu2);
     const float inv = den > 0.f ? 1.f / den : 0.f;
@@ -651,9 +674,37 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
           s[h][j] = ((unsigned)kidx <= rm.span) ? s[h][j] : kNegInf;
         }
     }
-    update_max<2>(s, sl2, m, l, o);
-    const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
-    float la[4] = {0.f, 0.f, 0.f, 0.f};
+    // block max: two chains of three-way maxima, then the other lane half
+    float mx0 = max3_raw(s[0][0], s[0][1], s[0][2]);
+    float mx1 = max3_raw(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+    for (int j = 3; j < 15; j += 2) {
+      mx0 = max3_raw(mx0, s[0][j], s[0][j + 1]);
+      mx1 = max3_raw(mx1, s[1][j], s[1][j + 1]);
+    }
+    mx0 = max3_raw(mx0, s[0][15], s[1][15]);
+    {
+      const float mx = max_raw(mx0, mx1);
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx0 = max_raw(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // the max moves only past the threshold (rare after a row's first valid
+    // key); lanes that keep theirs scale by exp2(0) = 1
+    const bool upd = (mx0 - m) * sl2 > kRescaleThreshold;
+    if (__any(upd)) {
+      const float mn = upd ? mx0 : m;
+      const float alpha = fast_exp2((m - mn) * sl2);
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
+      m = mn;
+    }
+    // (kMaxInit * sl2 is finite for every accepted scale; while no key is
+    // valid every score is -inf and every exponential 0)
+    const float mu2 = m * sl2;
+    float la[4];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -661,7 +712,7 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float e = fast_exp2(fmaf(s[h][8 * hh + i], sl2, -mu2));
-          la[i & 3] += e;
+          la[i & 3] = (h == 0 && hh == 0 && i < 4) ? e : la[i & 3] + e;
           pb[h][hh][i] = (T)e;
         }
     l += (la[0] + la[1]) + (la[2] + la[3]);
@@ -669,9 +720,10 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
   };
 
   // Block v streams into ring slot v % 4 and its page ids into id slot v % 4.
-  // Iteration t reads slots t-1 and t and, between its two turns, issues the
-  // K/V loads of block t+2 (4 loads, into the slot of block t-2) and then the ids
-  // of block t+6 (1 load), and moves the ids of block t+3 to registers. The
+  // Iteration t reads slots t-1 and t and issues the K/V loads of block t+2
+  // (4 loads, into the slot of block t-2) and then the ids of block t+6 (1
+  // load), and moves the ids of block t+3 to registers; waves 0-3 issue all of
+  // it around their M turn, so their softmax turn holds no load work. The
   // prologue issues what iterations -2 and -1 would have, after the sinks (LDS
   // copy, for the tiles' final normalisation) and the first tile's query.
   setup(cur);
@@ -750,15 +802,15 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
       top(t);
       dma_rows(t + 2, 0, e2);
       m_both(t);
+      dma_rows(t + 2, 1, e2);
+      load_ids(t + 6, e6);
+      read_ids(t + 3);
       ring_barrier();
       if (bnd) {
         finish(cur);
         cur = item_idx(ea);
         setup(cur);
       }
-      dma_rows(t + 2, 1, e2);
-      load_ids(t + 6, e6);
-      read_ids(t + 3);
       if (nq) {
         load_query(item_idx(eb));
         query_landed();

@@ -7,7 +7,7 @@ from serving_attention_amd import _lib
 
 
 def role_desc(qo_lens, kv_lens, page_size, causal=True, window_left=-1, keep=None,
-              qo_indptr=None, kv_indptr=None, last_page_len=None):
+              qo_indptr=None, kv_indptr=None, last_page_len=None, sm_scale=0.0):
     if qo_lens is None:
         return _lib.PodRoleDesc(0, None, None, None, int(causal), window_left, 0.0)
     qo = np.asarray(qo_indptr if qo_indptr is not None else np.concatenate([[0], np.cumsum(qo_lens)]), np.int32)
@@ -18,7 +18,7 @@ def role_desc(qo_lens, kv_lens, page_size, causal=True, window_left=-1, keep=Non
     lpl = np.asarray(last_page_len if last_page_len is not None else [(k - 1) % page_size + 1 for k in kv_lens], np.int32)
     keep.extend([qo, kv, lpl])
     p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    return _lib.PodRoleDesc(len(qo) - 1, p(qo), p(kv), p(lpl), int(causal), window_left, 0.0)
+    return _lib.PodRoleDesc(len(qo) - 1, p(qo), p(kv), p(lpl), int(causal), window_left, float(sm_scale))
 
 
 def plan_desc(prefill=None, decode=None, hqo=8, hkv=2, page_size=16, head_dim=128, dtype=1,

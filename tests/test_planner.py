@@ -304,6 +304,15 @@ def test_invalid_plan_parameters(case, code):
     assert rc == code
 
 
+@pytest.mark.parametrize("scale,code", [(1e6, _lib.POD_OK), (2e6, _lib.POD_ERR_INVALID),
+                                        (float("nan"), _lib.POD_ERR_INVALID)])
+def test_scale_range(scale, code):
+    # the query-tile softmax keeps scale * log2(e) * (-1e30) finite in fp32
+    desc, keep = plan_desc(prefill=dict(qo_lens=[10], kv_lens=[10], sm_scale=scale), hqo=8, hkv=2)
+    rc, _, _ = compute(desc)
+    assert rc == code
+
+
 @pytest.mark.parametrize("role", [dict(qo_indptr=[1, 10]),
                                   dict(qo_indptr=[0, 10], kv_indptr=[0, 0]),
                                   dict(last_page_len=[0]),
