@@ -226,6 +226,114 @@ def cpu_baseline(w, budget_s):
             "host_cpus": os.cpu_count(), "host": platform.processor() or platform.machine()}
 
 
+CASCADE = dict(prefix=1536, suffix=512, requests=128, num_qo_heads=64, num_kv_heads=8, page_size=16)
+
+
+def timed_events(fn, steps, warmup):
+    """Mean duration (us) of fn() over `steps` calls, HIP events on the current stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(s)
+        fn()
+        b.record(s)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / steps * 1e3
+
+
+def cascade_bench(args):
+    """Shared-prefix decode: 128 one-token requests whose 2048 keys are a shared
+    1536-token prefix plus 512 keys of their own (the decode shape of the `pod`
+    workload with three quarters of each context shared). Two-level cascade: one
+    fused launch (prefix as the prefill role over all 128 rows, suffixes as the
+    decode role) plus the merge, against the one-level decode that reads every
+    request's 2048 keys."""
+    import torch
+    from serving_attention_amd import BatchPOD, merge_states
+    from workloads import build_cascade
+    c = CASCADE
+    cw = build_cascade(c["prefix"], [c["suffix"]] * c["requests"], q_len=1,
+                       num_qo_heads=c["num_qo_heads"], num_kv_heads=c["num_kv_heads"],
+                       page_size=c["page_size"], device="cuda")
+    ws = torch.empty(128 << 20, dtype=torch.uint8, device="cuda")
+    kv = (cw.k_pool, cw.v_pool)
+    rows = int(cw.qo_indptr[-1])
+    H, D = c["num_qo_heads"], 128
+    kw = dict(num_qo_heads=H, num_kv_heads=c["num_kv_heads"], head_dim=D,
+              page_size=c["page_size"], dtype=torch.bfloat16)
+    idx_pre = torch.from_numpy(cw.prefix_indices).cuda()
+    idx_suf = torch.from_numpy(cw.suffix_indices).cuda()
+    idx_flat = torch.from_numpy(cw.flat_indices).cuda()
+    op, lp = torch.empty_like(cw.q), torch.empty(rows, H, device="cuda")
+    od, ld = torch.empty_like(cw.q), torch.empty(rows, H, device="cuda")
+    o, lse = torch.empty_like(cw.q), torch.empty(rows, H, device="cuda")
+
+    casc = BatchPOD(ws, "NHD", int_workspace_bytes=8 << 20)
+    casc.plan([0, rows], [0, len(cw.prefix_indices)], [cw.prefix_last_page_len],
+              cw.qo_indptr, cw.suffix_kv_indptr, cw.suffix_last_page_len,
+              causal_p=False, causal_d=True, **kw)
+
+    def run_pod():
+        casc.run(cw.q, kv, idx_pre, cw.q, kv, idx_suf, return_lse=True,
+                 out_p=op, lse_p=lp, out_d=od, lse_d=ld)
+
+    def run_merge():
+        merge_states(op, lp, od, ld, out=o, lse_out=lse)
+
+    def run_cascade():
+        run_pod()
+        run_merge()
+
+    t_casc = timed_events(run_cascade, args.steps, args.warmup)
+    t_pod = timed_events(run_pod, args.steps, args.warmup)
+    t_merge = timed_events(run_merge, args.steps, args.warmup)
+
+    ws2 = torch.empty(128 << 20, dtype=torch.uint8, device="cuda")
+    flat = BatchPOD(ws2, "NHD", int_workspace_bytes=8 << 20)
+    flat.plan(None, None, None, cw.qo_indptr, cw.flat_kv_indptr, cw.flat_last_page_len, causal_d=True, **kw)
+    fo, fl = torch.empty_like(cw.q), torch.empty(rows, H, device="cuda")
+    t_flat = timed_events(lambda: flat.run(None, None, None, cw.q, kv, idx_flat, return_lse=True,
+                                           out_d=fo, lse_d=fl), args.steps, args.warmup)
+    # the merge at streaming size (the cascade's own merge is launch-bound: 8192
+    # (row, head) pairs, 6 MB): 32768 rows x 64 heads, seeded N(0,1) states
+    big = 32768
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    ba = torch.randn(big, H, D, generator=gen, device="cuda").to(torch.bfloat16)
+    bb = torch.randn(big, H, D, generator=gen, device="cuda").to(torch.bfloat16)
+    bla = torch.randn(big, H, generator=gen, device="cuda")
+    blb = torch.randn(big, H, generator=gen, device="cuda")
+    bo, bl = torch.empty_like(ba), torch.empty_like(bla)
+    t_merge_big = timed_events(lambda: merge_states(ba, bla, bb, blb, out=bo, lse_out=bl),
+                               args.steps, args.warmup)
+    torch.cuda.synchronize()
+    # merge traffic: two O and two LSE in, one of each out (bf16 O, fp32 LSE)
+    merge_bytes = rows * H * (3 * D * 2 + 3 * 4)
+    big_bytes = big * H * (3 * D * 2 + 3 * 4)
+    kv_row = c["num_kv_heads"] * D * 2 * 2          # K and V bytes per token over all kv heads
+    print(json.dumps({
+        "metric": "shared-prefix decode step latency (us): two-level cascade vs one-level decode",
+        "value": t_casc, "unit": "us", "higher_is_better": False, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) values, shuffled pages)",
+        "config": {"workload": "cascade", "requests": c["requests"], "prefix": c["prefix"],
+                   "suffix": c["suffix"], "heads": f'{H}/{c["num_kv_heads"]}', "page_size": c["page_size"]},
+        "cascade_us": t_casc, "cascade_launch_us": t_pod, "merge_us": t_merge, "flat_decode_us": t_flat,
+        "speedup_vs_flat": t_flat / t_casc,
+        "kv_bytes_cascade": (c["prefix"] + c["requests"] * c["suffix"]) * kv_row,
+        "kv_bytes_flat": c["requests"] * (c["prefix"] + c["suffix"]) * kv_row,
+        "merge_bytes": merge_bytes,
+        "merge_roofline": {"bound": "hbm", "achieved": big_bytes / (t_merge_big * 1e-6) / 1e9,
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": big_bytes / (t_merge_big * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                           "bytes": big_bytes, "kernel_us": t_merge_big,
+                           "shape": f"{big} rows x {H} heads x {D}, bf16"},
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +351,9 @@ def main():
                     help="time launches that carry one role only (for per-role profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device copies (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--cascade", action="store_true",
+                    help="time the two-level shared-prefix cascade (one launch + merge) "
+                         "against the one-level decode over the same keys")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -252,6 +363,10 @@ def main():
 
     import torch
     from serving_attention_amd import BatchPOD
+
+    if args.cascade:
+        cascade_bench(args)
+        return
 
     if args.copy_calibration:
         a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")

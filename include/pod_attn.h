@@ -212,6 +212,29 @@ int pod_plan_stats(pod_ctx_t ctx, pod_plan_info* info);
  */
 int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream);
 
+/*
+ * Cascade merge of two attention states of the same rows over disjoint key
+ * sets, e.g. a shared-prefix level and a per-request level ([TOUR] core
+ * operator list, "Cascade Attention"; the base-2 LSE of [CUDNN] "LSE 契约" is
+ * what such a merge consumes). Per (row, head):
+ *   L = log2(2^lse_a + 2^lse_b),  O = 2^(lse_a - L) O_a + 2^(lse_b - L) O_b;
+ * a state with lse = -inf holds no keys and weighs 0; if both do, O = 0 and
+ * L = -inf. With `sinks` (device fp32 [num_heads], or NULL) the merged O is then
+ * divided by 1 + 2^(sink * log2(e) - L) and L is kept: the sink is applied once,
+ * so both inputs must be sink-free.
+ *   o_a, o_b, o_out  device, `dtype`, dense [rows, num_heads, head_dim], 16-byte
+ *                    aligned; o_out may be o_a or o_b itself (each element is
+ *                    read before it is written), no other overlap.
+ *   lse_a, lse_b, lse_out  device fp32 [rows, num_heads], 4-byte aligned; the
+ *                    same aliasing rule.
+ *   head_dim must be 128 (else POD_ERR_UNSUPPORTED); rows == 0 enqueues nothing.
+ * One kernel launch on `stream` of device `device`; asynchronous; allocates
+ * nothing. POD_ERR_INVALID for NULL buffers, negative sizes or misalignment.
+ */
+int pod_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                     void* o_out, float* lse_out, int64_t rows, int num_heads, int head_dim,
+                     int dtype, const float* sinks, int device, void* stream);
+
 /* Message for the calling thread's last failed call ("" if none). */
 const char* pod_last_error(void);
 

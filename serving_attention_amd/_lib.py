@@ -31,7 +31,7 @@ POD_IMAGE_MAGIC = 0x504F4431
 
 EXPORTED = (
     "pod_create", "pod_destroy", "pod_plan", "pod_plan_stats", "pod_run",
-    "pod_last_error", "pod_workspace_bytes", "pod_plan_compute",
+    "pod_last_error", "pod_workspace_bytes", "pod_plan_compute", "pod_merge_states",
 )
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -134,8 +134,11 @@ def load() -> ctypes.CDLL:
                                         ctypes.POINTER(ctypes.c_size_t)]
     lib.pod_plan_compute.argtypes = [ctypes.POINTER(PodPlanDesc), _i32p, ctypes.c_size_t,
                                      ctypes.POINTER(PodPlanInfo)]
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.pod_merge_states.argtypes = [vp, fp, vp, fp, vp, fp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, fp, ctypes.c_int, vp]
     for name in ("pod_create", "pod_destroy", "pod_plan", "pod_plan_stats", "pod_run",
-                 "pod_workspace_bytes", "pod_plan_compute"):
+                 "pod_workspace_bytes", "pod_plan_compute", "pod_merge_states"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib

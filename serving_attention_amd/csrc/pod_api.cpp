@@ -362,4 +362,31 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
   return POD_OK;
 }
 
+int pod_merge_states(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                     void* o_out, float* lse_out, int64_t rows, int num_heads, int head_dim,
+                     int dtype, const float* sinks, int device, void* stream) {
+  if (rows < 0 || num_heads <= 0) return set_err(POD_ERR_INVALID, "rows must be >= 0 and num_heads > 0");
+  if (head_dim != pod::kHeadDim) return set_err(POD_ERR_UNSUPPORTED, "head_dim must be 128");
+  if (dtype != POD_DTYPE_F16 && dtype != POD_DTYPE_BF16)
+    return set_err(POD_ERR_UNSUPPORTED, "dtype must be POD_DTYPE_F16 or POD_DTYPE_BF16");
+  if (rows == 0) {
+    g_err.clear();
+    return POD_OK;
+  }
+  if (!o_a || !o_b || !o_out || !lse_a || !lse_b || !lse_out)
+    return set_err(POD_ERR_INVALID, "o_a, lse_a, o_b, lse_b, o_out and lse_out are required");
+  for (const void* ptr : {o_a, o_b, (const void*)o_out})
+    if (reinterpret_cast<uintptr_t>(ptr) & 15) return set_err(POD_ERR_INVALID, "O buffers must be 16-byte aligned");
+  for (const void* ptr : {(const void*)lse_a, (const void*)lse_b, (const void*)lse_out, (const void*)sinks})
+    if (reinterpret_cast<uintptr_t>(ptr) & 3) return set_err(POD_ERR_INVALID, "LSE and sink buffers must be 4-byte aligned");
+  if (rows > INT64_MAX / 2 / num_heads / pod::kHeadDim) return set_err(POD_ERR_INVALID, "rows too large");
+  DeviceGuard dg(device);
+  if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
+  const int e = pod::launch_merge_states(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows * num_heads,
+                                         num_heads, dtype, sinks, stream);
+  if (e != (int)hipSuccess) return hip_err((hipError_t)e, "merge launch");
+  g_err.clear();
+  return POD_OK;
+}
+
 }  // extern "C"

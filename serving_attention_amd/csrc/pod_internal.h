@@ -93,5 +93,9 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
 // Launch the fused grid on `stream` (a hipStream_t); `done_event` (a hipEvent_t,
 // or null) is signalled when the launch completes. Returns a hipError_t value.
 int launch_pod_grid(const Params& p, int dtype, int grid, void* stream, void* done_event);
+// Cascade merge of n_pairs (row, head) states of head_dim 128 (merge_kernels.hip).
+int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb,
+                        void* oo, float* lo, int64_t n_pairs, int heads, int dtype,
+                        const float* sinks, void* stream);
 
 }  // namespace pod

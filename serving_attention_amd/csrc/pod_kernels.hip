@@ -1,9 +1,10 @@
 // Fused Prefill-On-Decode paged attention for gfx950 (MI355X, CDNA4).
 //
-// One launch runs every item of the planner's work list: query tiles (prefill
-// style: up to 128 rows share each K/V block staged in LDS) and key chunks
-// (decode style: the q_len x group rows of one request and kv head share every
-// K/V row read from HBM; keys are split over the 4 waves and over workgroups).
+// One launch of one persistent workgroup per CU runs the planner's work lists:
+// query tiles (prefill style: up to 256 rows share each K/V block staged in
+// LDS) and key chunks (decode style: the q_len x group rows of one request and
+// kv head share every K/V row read from HBM; keys are split over the 8 waves
+// and, for long requests, over workgroups).
 // This is the "prefill and decode in one launch" idea of the POD article
 // (www.dpshk.com/news/5405057, "POD 是什么"), built for wave64 and MFMA.
 //

@@ -256,3 +256,45 @@ def single_decode_with_kv_cache(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
         (_, _), (o, lse) = res
         return o.view(hq, d), lse.view(hq)
     return res[1].view(hq, d)
+
+
+def merge_states(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_b: torch.Tensor,
+                 sinks: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Cascade merge of two states of the same rows over disjoint key sets.
+
+    README tour, core operator list ("Cascade Attention": a shared-prefix level
+    and a per-request level); the base-2 LSE of the cuDNN article ("LSE 契约")
+    is what the merge consumes. o_* [rows, H, 128] float16 / bfloat16, lse_*
+    [rows, H] float32, all on one GPU. ``sinks`` [H] float32 is applied once to
+    the merged state (inputs must be sink-free). ``out`` / ``lse_out`` may be
+    an input tensor itself. Returns (out, lse_out).
+    """
+    for name, t in (("o_a", o_a), ("o_b", o_b)):
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [rows, heads, head_dim] tensor")
+    if o_b.shape != o_a.shape or o_b.dtype != o_a.dtype or o_b.device != o_a.device:
+        raise ValueError("o_a and o_b must match in shape, dtype and device")
+    rows, heads, d = o_a.shape
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
+        if t.shape != (rows, heads) or t.dtype != torch.float32 or not t.is_contiguous() \
+                or t.device != o_a.device:
+            raise ValueError(f"{name} must be a contiguous float32 [rows, heads] tensor on o_a's device")
+    if sinks is not None and (sinks.shape != (heads,) or sinks.dtype != torch.float32
+                              or not sinks.is_contiguous() or sinks.device != o_a.device):
+        raise ValueError("sinks must be a contiguous float32 [heads] tensor on o_a's device")
+    out = torch.empty_like(o_a) if out is None else out
+    lse_out = torch.empty_like(lse_a) if lse_out is None else lse_out
+    if out.shape != o_a.shape or out.dtype != o_a.dtype or not out.is_contiguous() or out.device != o_a.device:
+        raise ValueError("out must be a contiguous tensor like o_a")
+    if lse_out.shape != lse_a.shape or lse_out.dtype != torch.float32 or not lse_out.is_contiguous() \
+            or lse_out.device != o_a.device:
+        raise ValueError("lse_out must be a contiguous tensor like lse_a")
+    fp = ctypes.POINTER(ctypes.c_float)
+    f = lambda t: ctypes.cast(t.data_ptr(), fp) if t is not None else None
+    lib = _lib.load()
+    _lib.check(lib.pod_merge_states(o_a.data_ptr(), f(lse_a), o_b.data_ptr(), f(lse_b), out.data_ptr(),
+                                    f(lse_out), rows, heads, d, _dtype_code(o_a.dtype), f(sinks),
+                                    o_a.device.index if o_a.device.index is not None else 0,
+                                    _stream_handle(o_a.device)))
+    return out, lse_out

@@ -36,6 +36,21 @@ def test_null_arguments_are_rejected():
     out = ctypes.c_void_p()
     assert lib.pod_create(ctypes.byref(out), 0, None, 0, None, 0) == _lib.POD_ERR_INVALID
     assert lib.pod_plan_stats(None, None) == _lib.POD_ERR_INVALID
+    # the merge checks its arguments before touching a device
+    bf16 = _lib.POD_DTYPE_BF16
+    assert lib.pod_merge_states(None, None, None, None, None, None, 4, 8, 128, bf16, None, 0, None) \
+        == _lib.POD_ERR_INVALID
+    assert lib.pod_merge_states(None, None, None, None, None, None, 4, 8, 64, bf16, None, 0, None) \
+        == _lib.POD_ERR_UNSUPPORTED
+    assert lib.pod_merge_states(None, None, None, None, None, None, -1, 8, 128, bf16, None, 0, None) \
+        == _lib.POD_ERR_INVALID
+    assert lib.pod_merge_states(None, None, None, None, None, None, 0, 8, 128, bf16, None, 0, None) \
+        == _lib.POD_OK
+    bad = ctypes.c_void_p(0x1008)   # 8-byte aligned only
+    fl = ctypes.cast(ctypes.c_void_p(0x2000), ctypes.POINTER(ctypes.c_float))
+    assert lib.pod_merge_states(bad, fl, bad, fl, bad, fl, 4, 8, 128, bf16, None, 0, None) \
+        == _lib.POD_ERR_INVALID
+    assert b"16-byte" in lib.pod_last_error()
 
 
 def test_error_codes_map_to_python_exceptions():

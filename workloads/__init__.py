@@ -12,4 +12,6 @@ from .configs import (  # noqa: F401
     build,
     named_spec,
     NAMED,
+    CascadeWorkload,
+    build_cascade,
 )

@@ -294,3 +294,74 @@ def build(spec: WorkloadSpec, device="cpu", poison: bool = False) -> Workload:
     rt = {n: RoleTensors(**out[n]) for n, _ in roles}
     return Workload(spec=spec, prefill=rt.get("prefill"), decode=rt.get("decode"),
                     sinks=sinks, pools=list(pools.values()))
+
+
+@dataclass
+class CascadeWorkload:
+    """A shared-prefix decode batch (README tour, core operator list: "Cascade
+    Attention", a hierarchical KV cache whose shared prefix is stored once).
+
+    Every request's keys are the shared prefix followed by its own suffix; the
+    pool holds the prefix pages once. ``flat_*`` describes the same keys as one
+    page list per request (prefix pages, then its own), for the one-level
+    decode over the same data.
+    """
+    k_pool: torch.Tensor            # NHD [P, ps, H_kv, D]
+    v_pool: torch.Tensor
+    q: torch.Tensor                 # [rows, H_qo, D], rows of request b consecutive
+    sinks: Optional[torch.Tensor]
+    prefix_len: int
+    prefix_indices: np.ndarray      # int32 physical pages of the prefix
+    prefix_last_page_len: int
+    qo_indptr: np.ndarray           # int32 [B+1] decode rows
+    suffix_kv_indptr: np.ndarray    # int32 [B+1] pages of the suffixes
+    suffix_indices: np.ndarray
+    suffix_last_page_len: np.ndarray
+    flat_kv_indptr: np.ndarray      # int32 [B+1] pages of prefix + suffix
+    flat_indices: np.ndarray
+    flat_last_page_len: np.ndarray
+    num_qo_heads: int
+    num_kv_heads: int
+    page_size: int
+
+
+def build_cascade(prefix_len: int, suffix_lens: List[int], q_len: int = 1, num_qo_heads: int = 64,
+                  num_kv_heads: int = 8, page_size: int = 16, dtype: str = "bf16", sinks: bool = False,
+                  meta_seed: int = 7, value_seed: int = 1007, device="cpu") -> CascadeWorkload:
+    """Materialise a shared-prefix batch; the prefix fills whole pages, so the
+    flat page lists describe exactly the same keys."""
+    assert prefix_len % page_size == 0, "the prefix must fill whole pages"
+    assert all(s >= q_len for s in suffix_lens)
+    device = torch.device(device)
+    dt = _TORCH_DTYPES[dtype]
+    rng = np.random.default_rng(meta_seed)
+    n_pre = prefix_len // page_size
+    suf_pages = [_ceil_div(s, page_size) for s in suffix_lens]
+    total = n_pre + sum(suf_pages)
+    perm = rng.permutation(total).astype(np.int32)
+    pre_idx = perm[:n_pre]
+    suf_idx = perm[n_pre:]
+    suf_indptr = np.zeros(len(suffix_lens) + 1, dtype=np.int32)
+    suf_indptr[1:] = np.cumsum(suf_pages)
+    flat = [np.concatenate([pre_idx, suf_idx[suf_indptr[b]:suf_indptr[b + 1]]])
+            for b in range(len(suffix_lens))]
+    flat_indptr = np.zeros(len(suffix_lens) + 1, dtype=np.int32)
+    flat_indptr[1:] = np.cumsum([len(f) for f in flat])
+    lpl = np.array([(s - 1) % page_size + 1 for s in suffix_lens], dtype=np.int32)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(value_seed)
+    cache = torch.empty((total, 2, page_size, num_kv_heads, 128), dtype=dt, device=device)
+    _fill_randn_(cache, gen)
+    rows = q_len * len(suffix_lens)
+    q = torch.empty((rows, num_qo_heads, 128), dtype=dt, device=device)
+    _fill_randn_(q, gen)
+    sk = torch.randn(num_qo_heads, generator=gen, dtype=torch.float32, device=device) if sinks else None
+    k_pool, v_pool = cache.unbind(1)
+    return CascadeWorkload(
+        k_pool=k_pool, v_pool=v_pool, q=q, sinks=sk, prefix_len=prefix_len,
+        prefix_indices=pre_idx, prefix_last_page_len=page_size,
+        qo_indptr=np.arange(len(suffix_lens) + 1, dtype=np.int32) * q_len,
+        suffix_kv_indptr=suf_indptr, suffix_indices=suf_idx, suffix_last_page_len=lpl,
+        flat_kv_indptr=flat_indptr, flat_indices=np.concatenate(flat).astype(np.int32),
+        flat_last_page_len=lpl.copy(), num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads,
+        page_size=page_size)
