@@ -334,6 +334,60 @@ def cascade_bench(args):
     }))
 
 
+def graph_bench(args):
+    """Per-layer cost of run(): eager calls through the Python binding against
+    replays of one HIP graph captured from a graph-mode context (plan once, then
+    `layers` runs back to back, as a model's attention layers would call it).
+    Wall time per run with the GPU kept busy, so host overhead shows where the
+    kernel is short."""
+    import torch
+    from serving_attention_amd import BatchPOD
+    layers = 32
+    w = make_layers(args.workload, 1, "cuda")[0]
+    roles = tuple(n for n, _ in w.roles())
+    spec = w.spec
+    outs = alloc_outs(w, roles)
+    res = {}
+    for mode in ("eager", "graph"):
+        ws = torch.empty(128 << 20, dtype=torch.uint8, device="cuda")
+        kw = {}
+        if mode == "graph":
+            kw = dict(use_cuda_graph=True,
+                      prefill_batch_size=w.prefill.batch if w.prefill is not None else 0,
+                      decode_batch_size=w.decode.batch if w.decode is not None else 0)
+        pod = BatchPOD(ws, spec.kv_layout, int_workspace_bytes=8 << 20, **kw)
+        plan(pod, w, roles, args.decode_chunk, args.order)
+        run(pod, w, roles, outs)
+        torch.cuda.synchronize()
+        if mode == "graph":
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(layers):
+                    run(pod, w, roles, outs)
+            step = g.replay
+        else:
+            def step():
+                for _ in range(layers):
+                    run(pod, w, roles, outs)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        res[mode] = (time.perf_counter() - t0) / (args.steps * layers) * 1e6
+        del pod
+    print(json.dumps({
+        "metric": "attention run() cost per layer (us), eager calls vs graph replay",
+        "value": res["graph"], "unit": "us", "higher_is_better": False, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "layers_per_step": layers},
+        "eager_us_per_layer": res["eager"], "graph_us_per_layer": res["graph"],
+        "speedup": res["eager"] / res["graph"],
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -351,6 +405,9 @@ def main():
                     help="time launches that carry one role only (for per-role profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 1 GiB device copies (for scaling rocprofv3 byte counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time per-layer eager run() calls against replays of one captured graph "
+                         "(graph-mode context) on --workload")
     ap.add_argument("--cascade", action="store_true",
                     help="time the two-level shared-prefix cascade (one launch + merge) "
                          "against the one-level decode over the same keys")
@@ -366,6 +423,9 @@ def main():
 
     if args.cascade:
         cascade_bench(args)
+        return
+    if args.graph:
+        graph_bench(args)
         return
 
     if args.copy_calibration:

@@ -185,6 +185,28 @@ typedef struct pod_ctx* pod_ctx_t;
 int pod_create(pod_ctx_t* out, int device, void* float_ws, size_t float_ws_bytes,
                void* int_ws, size_t int_ws_bytes);
 
+/*
+ * Graph mode ([POD] "CUDAGraph 模式的运行时约束": the batch size is fixed when the
+ * wrapper is built and plan checks it). Like pod_create, plus:
+ *   - every pod_plan must have prefill.batch == prefill_batch and
+ *     decode.batch == decode_batch, and keep the first plan's heads, head_dim,
+ *     page_size, dtype, has_sinks, num_cus and each role's causal, window_left
+ *     and sm_scale; otherwise POD_ERR_INVALID;
+ *   - the work-list image lives at the start of int_ws (one image, so int_ws
+ *     needs only image_ints * 4 bytes) and pod_plan copies it on its `stream`;
+ *   - pod_run is one plain kernel launch of the full persistent grid with no
+ *     event operations: it can be captured into a HIP graph, and the captured
+ *     launch reads whatever plan was copied last, so a graph replays correctly
+ *     after any later plan on the same stream (the launch arguments carry only
+ *     buffer pointers and plan-time policy; what a plan decides is read from
+ *     the image). The caller keeps q, the K/V pools, kv_indices, out and lse at
+ *     the captured addresses and sizes them for the largest plan.
+ * pod_plan must still not be called during capture. batch sizes must be >= 0.
+ */
+int pod_create_graph(pod_ctx_t* out, int device, void* float_ws, size_t float_ws_bytes,
+                     void* int_ws, size_t int_ws_bytes, int32_t prefill_batch,
+                     int32_t decode_batch);
+
 /* Release the context's host state and staging buffers. NULL is accepted. */
 int pod_destroy(pod_ctx_t ctx);
 

@@ -32,6 +32,7 @@ POD_IMAGE_MAGIC = 0x504F4431
 EXPORTED = (
     "pod_create", "pod_destroy", "pod_plan", "pod_plan_stats", "pod_run",
     "pod_last_error", "pod_workspace_bytes", "pod_plan_compute", "pod_merge_states",
+    "pod_create_graph",
 )
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -124,6 +125,8 @@ def load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     vp = ctypes.c_void_p
     lib.pod_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, vp, ctypes.c_size_t]
+    lib.pod_create_graph.argtypes = [ctypes.POINTER(vp), ctypes.c_int, vp, ctypes.c_size_t, vp,
+                                     ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32]
     lib.pod_destroy.argtypes = [vp]
     lib.pod_plan.argtypes = [vp, ctypes.POINTER(PodPlanDesc), vp]
     lib.pod_plan_stats.argtypes = [vp, ctypes.POINTER(PodPlanInfo)]
@@ -138,7 +141,7 @@ def load() -> ctypes.CDLL:
     lib.pod_merge_states.argtypes = [vp, fp, vp, fp, vp, fp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, fp, ctypes.c_int, vp]
     for name in ("pod_create", "pod_destroy", "pod_plan", "pod_plan_stats", "pod_run",
-                 "pod_workspace_bytes", "pod_plan_compute", "pod_merge_states"):
+                 "pod_workspace_bytes", "pod_plan_compute", "pod_merge_states", "pod_create_graph"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib

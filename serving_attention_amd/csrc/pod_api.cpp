@@ -59,6 +59,13 @@ struct pod_ctx {
   hipStream_t copy_stream = nullptr;
   int next_staging = 0;
   int cur = 0;                                 // half of the current plan
+  // Graph mode (pod_create_graph): fixed batch sizes, one image at the start of
+  // the int workspace copied on the caller's stream, and the plan-time policy
+  // of the first plan kept, so a captured pod_run stays valid across plans.
+  bool graph = false;
+  int32_t fixed_batch[2] = {0, 0};
+  bool policy_set = false;
+  pod_plan_desc policy{};                      // first plan (resolved num_cus, scales)
 };
 
 namespace {
@@ -144,6 +151,19 @@ int pod_create(pod_ctx_t* out, int device, void* float_ws, size_t float_ws_bytes
   return POD_OK;
 }
 
+int pod_create_graph(pod_ctx_t* out, int device, void* float_ws, size_t float_ws_bytes, void* int_ws,
+                     size_t int_ws_bytes, int32_t prefill_batch, int32_t decode_batch) {
+  if (out) *out = nullptr;
+  if (prefill_batch < 0 || decode_batch < 0)
+    return set_err(POD_ERR_INVALID, "batch sizes must be >= 0");
+  const int rc = pod_create(out, device, float_ws, float_ws_bytes, int_ws, int_ws_bytes);
+  if (rc) return rc;
+  (*out)->graph = true;
+  (*out)->fixed_batch[0] = prefill_batch;
+  (*out)->fixed_batch[1] = decode_batch;
+  return POD_OK;
+}
+
 int pod_destroy(pod_ctx_t ctx) {
   if (!ctx) return POD_OK;
   {
@@ -170,9 +190,31 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   if (!desc) return set_err(POD_ERR_INVALID, "desc is NULL");
   pod_plan_desc d = *desc;
   if (d.num_cus <= 0) d.num_cus = ctx->num_cus;
+  if (ctx->graph) {
+    if (d.prefill.batch != ctx->fixed_batch[0] || d.decode.batch != ctx->fixed_batch[1])
+      return set_err(POD_ERR_INVALID, "graph context: batch sizes differ from the fixed ones (" +
+                                          std::to_string(ctx->fixed_batch[0]) + " prefill, " +
+                                          std::to_string(ctx->fixed_batch[1]) + " decode)");
+    if (ctx->policy_set) {
+      const pod_plan_desc& f = ctx->policy;
+      bool same = d.num_qo_heads == f.num_qo_heads && d.num_kv_heads == f.num_kv_heads &&
+                  d.head_dim == f.head_dim && d.page_size == f.page_size && d.dtype == f.dtype &&
+                  (d.has_sinks != 0) == (f.has_sinks != 0) && d.num_cus == f.num_cus;
+      const pod_role_desc* a[2] = {&d.prefill, &d.decode};
+      const pod_role_desc* b[2] = {&f.prefill, &f.decode};
+      for (int r = 0; r < 2; ++r)
+        same = same && (a[r]->causal != 0) == (b[r]->causal != 0) &&
+               a[r]->window_left == b[r]->window_left && a[r]->sm_scale == b[r]->sm_scale;
+      if (!same)
+        return set_err(POD_ERR_INVALID,
+                       "graph context: heads, head_dim, page_size, dtype, sinks, num_cus and each "
+                       "role's causal / window_left / sm_scale must stay those of the first plan");
+    }
+  }
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
-  (void)stream;   // the copy runs on the library's stream; pod_run waits for it
+  // the copy runs on the library's stream (pod_run waits for it), or in graph
+  // mode on `stream`, ordered with the launches there
   // The planner writes the image straight into a pinned staging buffer (two
   // alternate, each reused once its previous copy has completed).
   const int k = ctx->next_staging;
@@ -202,10 +244,11 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   int rc = pod::plan_compute(d, sink, inf, &err);
   if (rc) return set_err(rc, err);
   if (what) return hip_err(e, what);
-  if ((size_t)inf.int_ws_bytes > ctx->int_bytes)
-    return set_err(POD_ERR_WORKSPACE, "int workspace too small: need " +
-                                          std::to_string(inf.int_ws_bytes) + " bytes");
-  if (!ctx->copy_stream) {
+  // graph mode keeps one image; otherwise two alternate
+  const size_t need = ctx->graph ? bytes : (size_t)inf.int_ws_bytes;
+  if (need > ctx->int_bytes)
+    return set_err(POD_ERR_WORKSPACE, "int workspace too small: need " + std::to_string(need) + " bytes");
+  if (!ctx->graph && !ctx->copy_stream) {
     e = hipStreamCreateWithFlags(&ctx->copy_stream, hipStreamNonBlocking);
     if (e != hipSuccess) return hip_err(e, "hipStreamCreate");
   }
@@ -216,10 +259,25 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
     e = hipEventCreateWithFlags(&ctx->staged[k], hipEventDisableTiming);
     if (e != hipSuccess) return hip_err(e, "hipEventCreate");
   }
-  if (!ctx->used[k]) {   // a launch's stop event (hipExtLaunchKernel)
+  if (!ctx->graph && !ctx->used[k]) {   // a launch's stop event (hipExtLaunchKernel)
     e = hipEventCreate(&ctx->used[k]);
     if (e != hipSuccess) return hip_err(e, "hipEventCreate");
   }
+  if (ctx->graph) {
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    e = hipMemcpyAsync(ctx->int_ws, ctx->staging[k], bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (work list)");
+    e = hipEventRecord(ctx->staged[k], s);   // the staging buffer is free again after it
+    if (e != hipSuccess) return hip_err(e, "hipEventRecord");
+    ctx->staged_pending[k] = true;
+    ctx->next_staging = 1 - k;
+    if (!ctx->policy_set) {
+      ctx->policy = d;
+      ctx->policy.prefill.qo_indptr = ctx->policy.prefill.kv_indptr = ctx->policy.prefill.last_page_len = nullptr;
+      ctx->policy.decode.qo_indptr = ctx->policy.decode.kv_indptr = ctx->policy.decode.last_page_len = nullptr;
+      ctx->policy_set = true;
+    }
+  } else {
   // half k is free once the launches that read it (the plan before last) are
   // done; the host checks that (they normally are), so the copy stream carries
   // no wait on the launch stream
@@ -235,6 +293,7 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   ctx->staged_pending[k] = true;
   ctx->cur = k;
   ctx->next_staging = 1 - k;
+  }
 
   const pod_role_desc* rd[2] = {&d.prefill, &d.decode};
   for (int r = 0; r < 2; ++r) {
@@ -317,17 +376,7 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     o.causal = rp.causal;
     o.window_left = rp.window_left;
   }
-  int32_t* iws = int_half(ctx, ctx->cur);
-  p.reqs = iws + ctx->hdr[5];
-  p.items = iws + ctx->hdr[6];
-  p.wgs = iws + ctx->hdr[12];
-  p.blocks = iws + ctx->hdr[13];
-  p.tdesc = iws + ctx->hdr[18];
-  p.groups = iws + ctx->hdr[7];
-  p.counters = iws + ctx->hdr[8];
-  p.queue = iws + ctx->hdr[17];
-  p.pool_first = ctx->hdr[15];
-  p.pool_count = ctx->hdr[16];
+  p.image = ctx->graph ? reinterpret_cast<int32_t*>(ctx->int_ws) : int_half(ctx, ctx->cur);
   p.partials = reinterpret_cast<float*>(ctx->float_ws);
   p.sinks = args->sinks;
   p.num_qo_heads = ctx->num_qo_heads;
@@ -340,6 +389,14 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (ctx->graph) {
+    // the image copy went on the plan's stream, ahead of this launch; no event
+    // work, so the call can be captured into a graph
+    const int e = pod::launch_pod_grid(p, ctx->dtype, ctx->info.grid, stream, nullptr);
+    if (e != (int)hipSuccess) return hip_err((hipError_t)e, "pod grid launch");
+    g_err.clear();
+    return POD_OK;
+  }
   // this plan's work list must be up; a stream wait only while its copy runs
   hipError_t he = hipSuccess;
   if (ctx->staged_pending[ctx->cur]) {

@@ -37,6 +37,11 @@ constexpr int kMaxTilesPerWg = 65536;  // tile index fits the block-table entry
 //   {first key of the block, last key of its item, first page of the request, meta}
 // meta: bit 31 first block of its item, bit 30 role, bits 16..29 kv head,
 // bits 0..15 index of the item among the workgroup's query tiles.
+// Header words of the work-list image (the layout pod_attn.h documents).
+constexpr int kHdrReqs = 5, kHdrItems = 6, kHdrGroups = 7, kHdrCounters = 8, kHdrWgs = 12,
+              kHdrBlocks = 13, kHdrPoolFirst = 15, kHdrPoolCount = 16, kHdrQueue = 17,
+              kHdrTdesc = 18;
+
 constexpr uint32_t kEntFirst = 1u << 31;
 constexpr int kEntRoleShift = 30;
 constexpr int kEntKvhShift = 16;
@@ -63,17 +68,15 @@ struct RoleParams {
 
 struct Params {
   RoleParams role[2];
-  const int32_t* reqs;
-  const int32_t* items;
-  const int32_t* wgs;       // per workgroup: {first item, tiles, chunks, first block, blocks,
-                            //   chunks first, prefill tiles, prefill blocks}
-  const int32_t* blocks;    // query-tile block tables
-  const int32_t* tdesc;     // query-tile boundary data, one row per item
-  const int32_t* groups;
-  int32_t* counters;
-  int32_t* queue;           // {next pool item, workgroups done}; zero between launches
-  int32_t pool_first;       // shared key-chunk pool: items [pool_first, pool_first + pool_count)
-  int32_t pool_count;
+  // The work-list image in device memory. Everything a plan decides is read
+  // from it (header words give the region offsets and the pool range), so the
+  // launch arguments stay valid when a later plan rewrites the image in place:
+  //   reqs, items, wgs (per workgroup: {first item, tiles, chunks, first block,
+  //   blocks, chunks first, prefill tiles, prefill blocks}), blocks (query-tile
+  //   block tables), tdesc (query-tile boundary rows), groups, counters and the
+  //   queue {next pool item, workgroups done} (zero between launches); the
+  //   shared key-chunk pool is items [pool_first, pool_first + pool_count).
+  int32_t* image;
   float* partials;
   const float* sinks;       // nullptr = no sinks
   int32_t num_qo_heads;

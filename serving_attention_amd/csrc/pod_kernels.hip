@@ -378,6 +378,10 @@ using CI32 = const __attribute__((address_space(4))) int32_t;
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 using CI32x4 = const __attribute__((address_space(4))) i32x4;
 __device__ __forceinline__ CI32* plan_words(const int32_t* p) { return (CI32*)p; }
+// header word i of the work-list image (uniform: one scalar load)
+__device__ __forceinline__ int hdr_word(PArg p, int i) { return plan_words(p.image)[i]; }
+// image region whose offset is header word i
+__device__ __forceinline__ int32_t* image_region(PArg p, int i) { return p.image + hdr_word(p, i); }
 
 // one query-tile item, wave-uniform (its boundary row of the plan: one
 // 32-byte scalar load)
@@ -411,7 +415,7 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
   const char* const vpool = r.v;
   const bool paged = r.indices != nullptr;
   // page-id loads read the page table, or word 0 of the request table (unused)
-  const int32_t* const id_src = paged ? r.indices : p.reqs;
+  const int32_t* const id_src = paged ? r.indices : image_region(p, kHdrReqs);
   const uint32_t kv_sp = r.kv_sp_b, kv_st = r.kv_st_b;
   const uint32_t kv_sh = role ? p.role[1].kv_sh_b : p.role[0].kv_sh_b;
 
@@ -1084,36 +1088,45 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
       reinterpret_cast<u32x4*>(op)[1] = __builtin_bit_cast(u32x4, w1);
       if (lse_p && (tid & 7) == 0) *lse_p = lse_r;
     } else {
-      const int first_slot = p.groups[grp * kGroupWords + 1];
+      const int first_slot = image_region(p, kHdrGroups)[grp * kGroupWords + 1];
       float* slot = p.partials + (int64_t)(first_slot + split) * kSlotFloats;
       const float inv = L > 0.f ? 1.f / L : 0.f;
-      float4* dst = reinterpret_cast<float4*>(slot + frow * kHeadDim + d0);
+      // die-coherent stores (sc1: relaxed atomics at agent scope), so the last
+      // workgroup of the group reads them from any die without an L2 writeback
+      float* dst = slot + frow * kHeadDim + d0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        dst[i] = make_float4(vals[4 * i] * inv, vals[4 * i + 1] * inv, vals[4 * i + 2] * inv,
-                             vals[4 * i + 3] * inv);
-      if ((tid & 7) == 0) slot[kChunkRows * kHeadDim + frow] = lse_r;
+      for (int i = 0; i < 16; ++i)
+        __hip_atomic_store(dst + i, vals[i] * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((tid & 7) == 0)
+        __hip_atomic_store(slot + kChunkRows * kHeadDim + frow, lse_r, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   if (grp < 0) return;
 
   // ---- split-KV: the last workgroup of the group merges every partial state
-  const int n_splits = p.groups[grp * kGroupWords + 0];
-  const int first_slot = p.groups[grp * kGroupWords + 1];
-  __threadfence();
+  const int32_t* groups = image_region(p, kHdrGroups);
+  const int n_splits = groups[grp * kGroupWords + 0];
+  const int first_slot = groups[grp * kGroupWords + 1];
+  // Publication without fences: every partial went out with a die-coherent
+  // store; each thread waits until its stores have completed, the workgroup
+  // syncs, and only then is the group's counter bumped. The last arriver reads
+  // the partials with die-coherent loads. (An agent-scope release fence would
+  // write back the die's whole L2, every key block of it included.)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
-    const int prev = atomicAdd(&p.counters[grp], 1);
+    const int prev = atomicAdd(image_region(p, kHdrCounters) + grp, 1);
     *sm_flag = (prev == n_splits - 1);
   }
   __syncthreads();
   if (!*sm_flag) return;
-  __threadfence();
+  auto ld_c = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   if (fok) {
     const float* base = p.partials + (int64_t)first_slot * kSlotFloats;
     float Mx = kNegInf;
     for (int s = 0; s < n_splits; ++s)
-      Mx = fmaxf(Mx, base[(int64_t)s * kSlotFloats + kChunkRows * kHeadDim + frow]);
+      Mx = fmaxf(Mx, ld_c(base + (int64_t)s * kSlotFloats + kChunkRows * kHeadDim + frow));
     float acc16[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc16[i] = 0.f;
@@ -1121,17 +1134,11 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
     if (Mx != kNegInf) {
       for (int s = 0; s < n_splits; ++s) {
         const float* sl = base + (int64_t)s * kSlotFloats;
-        const float w = fast_exp2(sl[kChunkRows * kHeadDim + frow] - Mx);
+        const float w = fast_exp2(ld_c(sl + kChunkRows * kHeadDim + frow) - Mx);
         tot += w;
-        const float4* src = reinterpret_cast<const float4*>(sl + frow * kHeadDim + d0);
+        const float* src = sl + frow * kHeadDim + d0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 x = src[i];
-          acc16[4 * i] += w * x.x;
-          acc16[4 * i + 1] += w * x.y;
-          acc16[4 * i + 2] += w * x.z;
-          acc16[4 * i + 3] += w * x.w;
-        }
+        for (int i = 0; i < 16; ++i) acc16[i] += w * ld_c(src + i);
       }
     }
     const float L = tot > 0.f ? Mx + fast_log2(tot) : kNegInf;
@@ -1147,7 +1154,7 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
     reinterpret_cast<u32x4*>(op)[1] = __builtin_bit_cast(u32x4, w1);
     if (lse_p && (tid & 7) == 0) *lse_p = L;
   }
-  if (tid == 0) atomicExch(&p.counters[grp], 0);
+  if (tid == 0) atomicExch(image_region(p, kHdrCounters) + grp, 0);
 }
 
 // One persistent workgroup per CU runs its static list from the plan: its key
@@ -1168,16 +1175,16 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
   __shared__ int pool_slot;
   // destination of the block-table prefetch
   __shared__ __attribute__((aligned(16))) char pf_lds[256];
-  CI32* wg = plan_words(p.wgs) + blockIdx.x * kWgWords;
+  CI32* wg = plan_words(image_region(p, kHdrWgs)) + blockIdx.x * kWgWords;
   const int first_item = wg[0], n_tiles = wg[1], n_chunks = wg[2];
   const int first_blk = wg[3], n_blk = wg[4];
   const bool chunks_first = wg[5] != 0;
   auto run_chunk = [&](int idx) __attribute__((always_inline)) {
-    CI32* it = plan_words(p.items) + idx * kItemWords;
+    CI32* it = plan_words(image_region(p, kHdrItems)) + idx * kItemWords;
     const int flags = it[0];
     const int kvh = it[2], kv_begin = it[5], kv_end = it[6], grp = it[7];
     const RoleView r = pick_role(p, flags & kFlagRole, kvh);
-    CI32* rq = plan_words(p.reqs) + it[1] * kReqWords;
+    CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
     const RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
     chunk_item<T>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds);
   };
@@ -1190,9 +1197,9 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
   if (chunks_first) run_chunks();
   if (n_tiles > 0) {
     __syncthreads();
-    const int32_t* ttd = p.tdesc + (int64_t)first_item * kTdescWords;
+    const int32_t* ttd = image_region(p, kHdrTdesc) + (int64_t)first_item * kTdescWords;
     const int pre_tiles = wg[6];
-    const int32_t* tb = p.blocks + (int64_t)first_blk * kBlockWords;
+    const int32_t* tb = image_region(p, kHdrBlocks) + (int64_t)first_blk * kBlockWords;
     // one block stream per role: the prefill tiles, then the decode tiles
     const int pre_blk = wg[7];
     for (int role = 0; role < 2; ++role) {
@@ -1207,20 +1214,22 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
     }
   }
   if (!chunks_first) run_chunks();
-  if (p.pool_count > 0) {
+  const int pool_count = hdr_word(p, kHdrPoolCount);
+  if (pool_count > 0) {
+    int32_t* queue = image_region(p, kHdrQueue);
     for (;;) {
       __syncthreads();   // the previous item is done with the LDS and pool_slot
-      if (threadIdx.x == 0) pool_slot = atomicAdd(p.queue, 1);
+      if (threadIdx.x == 0) pool_slot = atomicAdd(queue, 1);
       __syncthreads();
       const int j = __builtin_amdgcn_readfirstlane(pool_slot);
-      if (j >= p.pool_count) break;
-      run_chunk(p.pool_first + j);
+      if (j >= pool_count) break;
+      run_chunk(hdr_word(p, kHdrPoolFirst) + j);
     }
     // every workgroup has taken its last (empty) turn before it counts itself
     // done, so the last one can clear both counters
-    if (threadIdx.x == 0 && atomicAdd(p.queue + 1, 1) == (int)gridDim.x - 1) {
-      atomicExch(p.queue, 0);
-      atomicExch(p.queue + 1, 0);
+    if (threadIdx.x == 0 && atomicAdd(queue + 1, 1) == (int)gridDim.x - 1) {
+      atomicExch(queue, 0);
+      atomicExch(queue + 1, 0);
     }
   }
 }
@@ -1231,6 +1240,13 @@ int launch_pod_grid(const Params& p, int dtype, int grid, void* stream, void* do
   if (grid <= 0) return (int)hipSuccess;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipEvent_t done = reinterpret_cast<hipEvent_t>(done_event);
+  if (!done) {   // a plain dispatch (capturable into a graph)
+    if (dtype == POD_DTYPE_BF16)
+      hipLaunchKernelGGL(pod_grid_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL(pod_grid_kernel<_Float16>, dim3(grid), dim3(kThreads), 0, s, p);
+    return (int)hipGetLastError();
+  }
   // the completion event rides on the dispatch itself (no separate marker)
   if (dtype == POD_DTYPE_BF16)
     hipExtLaunchKernelGGL(pod_grid_kernel<__bf16>, dim3(grid), dim3(kThreads), 0, s, nullptr, done, 0, p);

@@ -75,7 +75,12 @@ class BatchPOD:
     """Batch prefill + batch decode paged attention in one launch per run()."""
 
     def __init__(self, float_workspace_buffer: torch.Tensor, kv_layout: str = "NHD",
-                 int_workspace_bytes: int = 8 << 20):
+                 int_workspace_bytes: int = 8 << 20, use_cuda_graph: bool = False,
+                 prefill_batch_size: Optional[int] = None, decode_batch_size: Optional[int] = None):
+        """``use_cuda_graph`` fixes both batch sizes (POD article, "CUDAGraph 模式的运行时
+        约束"): every plan must keep them, run() may be captured into a graph and
+        the graph replays correctly after later plans. The caller then passes
+        q, out and lse buffers sized for the largest plan and keeps them."""
         self._lib = _lib.load()
         if not float_workspace_buffer.is_cuda:
             raise ValueError("the float workspace must be a device tensor")
@@ -86,10 +91,17 @@ class BatchPOD:
         self._float_ws = float_workspace_buffer
         self._int_ws = torch.zeros(int_workspace_bytes // 4, dtype=torch.int32, device=self.device)
         ctx = ctypes.c_void_p()
-        _lib.check(self._lib.pod_create(
-            ctypes.byref(ctx), self.device.index if self.device.index is not None else 0,
-            ctypes.c_void_p(self._float_ws.data_ptr()), self._float_ws.numel() * self._float_ws.element_size(),
-            ctypes.c_void_p(self._int_ws.data_ptr()), self._int_ws.numel() * 4))
+        dev = self.device.index if self.device.index is not None else 0
+        fws = (ctypes.c_void_p(self._float_ws.data_ptr()), self._float_ws.numel() * self._float_ws.element_size())
+        iws = (ctypes.c_void_p(self._int_ws.data_ptr()), self._int_ws.numel() * 4)
+        self.use_cuda_graph = bool(use_cuda_graph)
+        if self.use_cuda_graph:
+            if prefill_batch_size is None or decode_batch_size is None:
+                raise ValueError("use_cuda_graph needs prefill_batch_size and decode_batch_size")
+            _lib.check(self._lib.pod_create_graph(ctypes.byref(ctx), dev, *fws, *iws,
+                                                  int(prefill_batch_size), int(decode_batch_size)))
+        else:
+            _lib.check(self._lib.pod_create(ctypes.byref(ctx), dev, *fws, *iws))
         self._ctx = ctx
         self._planned = None
 
@@ -154,7 +166,9 @@ class BatchPOD:
         if rows == 0 or q is None:
             return _lib.PodRoleArgs()
         hq, d = pl["num_qo_heads"], pl["head_dim"]
-        if q.dim() != 3 or q.shape[0] != rows or q.shape[1] != hq or q.shape[2] != d:
+        # graph mode: buffers sized for the largest plan
+        short = q.shape[0] < rows if self.use_cuda_graph else q.shape[0] != rows
+        if q.dim() != 3 or short or q.shape[1] != hq or q.shape[2] != d:
             raise ValueError(f"q must be [{rows}, {hq}, {d}], got {tuple(q.shape)}")
         if _DT.get(q.dtype) != pl["dtype"]:
             raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "q dtype differs from the planned dtype")
@@ -198,10 +212,11 @@ class BatchPOD:
                 outs.append(None)
                 lses.append(None)
                 continue
+            n = q.shape[0] if self.use_cuda_graph else rows
             if o is None:
-                o = torch.empty((rows, hq, d), dtype=q.dtype, device=q.device)
+                o = torch.empty((n, hq, d), dtype=q.dtype, device=q.device)
             if l is None and return_lse:
-                l = torch.empty((rows, hq), dtype=torch.float32, device=q.device)
+                l = torch.empty((n, hq), dtype=torch.float32, device=q.device)
             outs.append(o)
             lses.append(l)
         if pl["sinks"]:

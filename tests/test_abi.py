@@ -36,6 +36,9 @@ def test_null_arguments_are_rejected():
     out = ctypes.c_void_p()
     assert lib.pod_create(ctypes.byref(out), 0, None, 0, None, 0) == _lib.POD_ERR_INVALID
     assert lib.pod_plan_stats(None, None) == _lib.POD_ERR_INVALID
+    assert lib.pod_create_graph(None, 0, None, 0, None, 0, 1, 1) == _lib.POD_ERR_INVALID
+    assert lib.pod_create_graph(ctypes.byref(out), 0, None, 0, None, 0, -1, 1) == _lib.POD_ERR_INVALID
+    assert b"batch" in lib.pod_last_error()
     # the merge checks its arguments before touching a device
     bf16 = _lib.POD_DTYPE_BF16
     assert lib.pod_merge_states(None, None, None, None, None, None, 4, 8, 128, bf16, None, 0, None) \
