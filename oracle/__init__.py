@@ -20,4 +20,6 @@ from .attend import (  # noqa: F401
     attend_role_dense,
     merge_states,
     apply_sink,
+    e4m3_to_float,
+    attend_rows_fp8_scaled,
 )

@@ -225,3 +225,36 @@ def apply_sink(o, lse, sink):
     lse = np.asarray(lse, dtype=np.float64)
     sink = np.asarray(sink, dtype=np.float64)
     return o / (1.0 + np.exp(sink - lse * LN2))[..., None]
+
+
+def e4m3_to_float(codes) -> np.ndarray:
+    """Decode FP8 E4M3 bytes ("fn" variant: no infinities) to float64.
+
+    Format: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits.
+    Exponent field 0 holds the subnormals m/8 * 2^-6; every other field is
+    (1 + m/8) * 2^(e - 7); only exponent 15 with mantissa 7 is NaN, so the
+    largest finite magnitude is 1.75 * 2^8 = 448. This is the FP8 KV-cache
+    element type whose calibration scales the POD article's run parameters
+    (q_scale / k_scale / v_scale, "Prefill 侧参数") describe.
+    """
+    b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b >> 7, -1.0, 1.0)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def attend_rows_fp8_scaled(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
+                           sm_scale: float, q_scale: float, k_scale: float, v_scale: float,
+                           sinks: Optional[np.ndarray] = None):
+    """Decode attention over an FP8 KV cache with calibration scales (POD
+    article, "Prefill 侧参数": q_scale and k_scale multiply into the decode
+    sm_scale; v_scale multiplies the decode output after the kernel).
+
+    k, v hold the decoded FP8 values (float64). Returns O [n, H_qo, D] and the
+    base-2 lse (sink excluded) of the scaled scores.
+    """
+    o, lse = attend_rows(q, k, v, keep, sm_scale * q_scale * k_scale, sinks)
+    return o * v_scale, lse

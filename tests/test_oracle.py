@@ -371,3 +371,42 @@ def test_validation_rejects_bad_page_tables():
         run(dict(inp, last_page_len=np.array([0])), causal=True)
     with pytest.raises(oracle.OracleInputError):
         run(dict(inp, qo_indptr=np.array([0, 11])), causal=True)   # q_len > kv_len
+
+
+def test_e4m3_decoding_matches_torch_float8_e4m3fn():
+    # every one of the 256 codes against torch's own float8_e4m3fn -> float32
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_to_float(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(ours[fin], ref[fin])
+    assert np.isnan(ours).sum() == 2                      # 0x7F and 0xFF only
+
+
+def test_e4m3_closed_form_values():
+    v = oracle.e4m3_to_float(np.array([0x38, 0x7E, 0x01, 0x08, 0xB8, 0x00, 0x80, 0x3C], np.uint8))
+    assert v[0] == 1.0                                    # exponent field 7, mantissa 0
+    assert v[1] == 448.0                                  # largest finite: 1.75 * 2^8
+    assert v[2] == 2.0 ** -9                              # smallest subnormal: 1/8 * 2^-6
+    assert v[3] == 2.0 ** -6                              # smallest normal
+    assert v[4] == -1.0
+    assert v[5] == 0.0 and v[6] == 0.0 and np.signbit(v[6])
+    assert v[7] == 1.5
+
+
+def test_fp8_scales_fold_into_scale_and_output():
+    # q_scale * k_scale act as a factor on the scores, v_scale on the output:
+    # the same as scaling K and V themselves
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((3, 4, 128))
+    k = rng.standard_normal((50, 2, 128))
+    v = rng.standard_normal((50, 2, 128))
+    keep = oracle.valid_key_mask(3, 50, True, -1)
+    o1, l1 = oracle.attend_rows_fp8_scaled(q, k, v, keep, 0.09, 0.5, 3.0, 1.75)
+    o2, l2 = attend_rows(q, k * 1.5, v * 1.75, keep, 0.09)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+    o3, l3 = oracle.attend_rows_fp8_scaled(q, k, v, keep, 0.09, 1.0, 1.0, 1.0)
+    o4, l4 = attend_rows(q, k, v, keep, 0.09)
+    assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
