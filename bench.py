@@ -37,6 +37,8 @@ DESCR = {
            "64/8 heads, head_dim 128, page_size 1, bf16",
     "pod_chunked": "chunked-prefill POD: 4096-token chunk on a 16384-token prefix + 256 x 4-token "
                    "decode (kv 1024..32768), window_left 4096, fp32 sinks, 64/8 heads, page_size 16, bf16",
+    "pod_fp8": "POD fused step as `pod` with the decode K/V cache in FP8 E4M3 (q_scale 1, "
+               "k_scale 0.75, v_scale 1.25); q, prefill K/V and outputs bf16",
 }
 
 
@@ -48,6 +50,7 @@ def work_counts(w):
     eb = 2
     out = {}
     for name, r in w.roles():
+        kv_eb = 1 if (name == "decode" and spec.decode_kv_dtype == "fp8_e4m3") else eb
         pairs = 0
         kv_tokens = 0
         for qo, kv in zip(r.qo_lens, r.kv_lens):
@@ -64,7 +67,7 @@ def work_counts(w):
             kv_tokens += last_hi - lo_first + 1
         rows = sum(r.qo_lens)
         flops = 4.0 * D * Hq * pairs
-        kv_bytes = float(kv_tokens) * Hk * D * 2 * eb
+        kv_bytes = float(kv_tokens) * Hk * D * 2 * kv_eb
         io_bytes = rows * Hq * D * eb * 2 + rows * Hq * 4
         out[name] = dict(flops=flops, kv_bytes=kv_bytes, io_bytes=io_bytes, rows=rows)
     return out
@@ -114,7 +117,8 @@ def plan(pod, w, roles, decode_chunk, order):
              causal_p=p.causal if p else True, causal_d=d.causal if d else True,
              window_left_p=p.window_left if p else -1, window_left_d=d.window_left if d else -1,
              sm_scale_p=p.sm_scale if p else None, sm_scale_d=d.sm_scale if d else None,
-             sinks=spec.sinks, decode_chunk=decode_chunk, order=order)
+             sinks=spec.sinks, decode_chunk=decode_chunk, order=order,
+             kv_dtype_d=torch.float8_e4m3fn if (d and spec.decode_kv_dtype == "fp8_e4m3") else None)
 
 
 def run(pod, w, roles, outs):
@@ -123,7 +127,15 @@ def run(pod, w, roles, outs):
     return pod.run(p.q if p else None, p.kv_cache if p else None, p.kv_indices_dev if p else None,
                    d.q if d else None, d.kv_cache if d else None, d.kv_indices_dev if d else None,
                    sinks=w.sinks if w.spec.sinks else None, return_lse=True,
-                   out_p=outs[0][0], lse_p=outs[0][1], out_d=outs[1][0], lse_d=outs[1][1])
+                   out_p=outs[0][0], lse_p=outs[0][1], out_d=outs[1][0], lse_d=outs[1][1],
+                   **fp8_args(w.spec, d is not None))
+
+
+def fp8_args(spec, has_decode):
+    if not has_decode or spec.decode_kv_dtype != "fp8_e4m3":
+        return {}
+    qs, ks, vs = spec.fp8_scales
+    return dict(q_scale_d=qs, k_scale_d=ks, v_scale_d=vs)
 
 
 def alloc_outs(w, roles):
@@ -203,8 +215,12 @@ def cpu_baseline(w, budget_s):
                 break
             p0, p1 = int(r.kv_indptr[b]), int(r.kv_indptr[b + 1])
             idx = torch.from_numpy(r.kv_indices[p0:p1].astype(np.int64)).to(r.k_pool.device)
-            kp = r.k_pool.index_select(0, idx).float().cpu().numpy()
-            vp = r.v_pool.index_select(0, idx).float().cpu().numpy()
+            if r.k_pool.dtype == torch.float8_e4m3fn:   # the oracle decodes FP8 itself
+                kp = oracle.e4m3_to_float(r.k_pool.view(torch.uint8).index_select(0, idx).cpu().numpy())
+                vp = oracle.e4m3_to_float(r.v_pool.view(torch.uint8).index_select(0, idx).cpu().numpy())
+            else:
+                kp = r.k_pool.index_select(0, idx).float().cpu().numpy()
+                vp = r.v_pool.index_select(0, idx).float().cpu().numpy()
             q0, q1 = int(r.qo_indptr[b]), int(r.qo_indptr[b + 1])
             q = r.q[q0:q1].float().cpu().numpy()
             qo = q1 - q0

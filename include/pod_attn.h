@@ -46,7 +46,7 @@ enum {
   POD_ERR_HIP = 5           /* a HIP runtime call failed (message in pod_last_error) */
 };
 
-enum { POD_DTYPE_F16 = 0, POD_DTYPE_BF16 = 1 };
+enum { POD_DTYPE_F16 = 0, POD_DTYPE_BF16 = 1, POD_DTYPE_FP8_E4M3 = 3 };
 
 /* Item order policies for the fused grid (see pod_plan_desc.order). */
 enum {
@@ -106,6 +106,16 @@ typedef struct pod_role_desc {
  *                 cost, decode slightly ahead; PREFILL_FIRST / DECODE_FIRST run one
  *                 role's items before the other's; LONGEST_FIRST takes the items of
  *                 both roles heaviest first. Any other value is POD_ERR_INVALID.
+ *   decode_kv_dtype  element type of the decode role's K/V pools: 0 = `dtype`, or
+ *                 POD_DTYPE_FP8_E4M3 (OCP E4M3, 1 byte, strides still in elements):
+ *                 the FP8 KV cache whose calibration scales the POD article lists
+ *                 with the decode run parameters ([POD] "Prefill 侧参数"). q and O stay
+ *                 `dtype`; values are widened exactly to `dtype` inside the launch.
+ *                 Supported only where every decode (request, kv head) runs as one
+ *                 key-chunk item, i.e. q_len * group <= 32 rows (POD_ERR_UNSUPPORTED
+ *                 otherwise). The prefill role keeps `dtype` K/V. An FP8 decode role
+ *                 needs kv_indices at pod_run (POD_ERR_INVALID for NULL) and K/V strides
+ *                 that are multiples of 16 elements.
  */
 typedef struct pod_plan_desc {
   pod_role_desc prefill;
@@ -119,6 +129,7 @@ typedef struct pod_plan_desc {
   int32_t num_cus;
   int32_t decode_chunk;
   int32_t order;
+  int32_t decode_kv_dtype;
 } pod_plan_desc;
 
 /*
@@ -153,11 +164,21 @@ typedef struct pod_role_args {
   float* lse;
 } pod_role_args;
 
-/* sinks: device fp32 [num_qo_heads]; required iff the plan had has_sinks. */
+/*
+ * sinks: device fp32 [num_qo_heads]; required iff the plan had has_sinks.
+ * q_scale_d, k_scale_d, v_scale_d: the decode role's calibration scales for an
+ * FP8 KV cache ([POD] "Prefill 侧参数"): q_scale_d * k_scale_d multiply the
+ * decode sm_scale, v_scale_d multiplies the decode output (folded into the
+ * launch's final normalisation, before the cast to `dtype`; the LSE does not
+ * see it). 0 means 1.0; any value is accepted for any decode_kv_dtype.
+ */
 typedef struct pod_run_args {
   pod_role_args prefill;
   pod_role_args decode;
   const float* sinks;
+  float q_scale_d;
+  float k_scale_d;
+  float v_scale_d;
 } pod_run_args;
 
 /* Counts of what a plan holds (filled by pod_plan_compute / pod_plan_stats). */

@@ -20,6 +20,7 @@ POD_ERR_HIP = 5
 
 POD_DTYPE_F16 = 0
 POD_DTYPE_BF16 = 1
+POD_DTYPE_FP8_E4M3 = 3
 
 POD_ORDER_INTERLEAVE = 0
 POD_ORDER_PREFILL_FIRST = 1
@@ -63,6 +64,7 @@ class PodPlanDesc(ctypes.Structure):
         ("num_cus", ctypes.c_int32),
         ("decode_chunk", ctypes.c_int32),
         ("order", ctypes.c_int32),
+        ("decode_kv_dtype", ctypes.c_int32),
     ]
 
 
@@ -89,6 +91,9 @@ class PodRunArgs(ctypes.Structure):
         ("prefill", PodRoleArgs),
         ("decode", PodRoleArgs),
         ("sinks", ctypes.c_void_p),
+        ("q_scale_d", ctypes.c_float),
+        ("k_scale_d", ctypes.c_float),
+        ("v_scale_d", ctypes.c_float),
     ]
 
 

@@ -160,6 +160,14 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
   };
   auto is_chunk = [&](const Req& q) { return (int64_t)q.qo_len * g <= kChunkRows; };
 
+  if (d.decode_kv_dtype != 0 && d.decode_kv_dtype != d.dtype && d.decode_kv_dtype != POD_DTYPE_FP8_E4M3)
+    return fail(err, POD_ERR_UNSUPPORTED, "decode_kv_dtype must be 0, dtype or POD_DTYPE_FP8_E4M3");
+  if (d.decode_kv_dtype == POD_DTYPE_FP8_E4M3)
+    for (const Req& q : reqs)
+      if (q.role == 1 && q.qo_len > 0 && !is_chunk(q))
+        return fail(err, POD_ERR_UNSUPPORTED,
+                    "FP8 decode K/V needs q_len * group <= 32 rows per request (key-chunk items)");
+
   // decode split size: enough key-chunk items for ~4 per CU, at least 256 keys each
   int64_t chunk_keys_total = 0;
   for (const Req& q : reqs)

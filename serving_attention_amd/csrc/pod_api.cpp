@@ -45,6 +45,7 @@ struct pod_ctx {
   bool planned = false;
   RolePlan role[2];
   int32_t num_qo_heads = 0, num_kv_heads = 0, page_size = 0, dtype = 0, has_sinks = 0;
+  bool decode_kv_fp8 = false;
   pod_plan_info info{};
   int32_t hdr[POD_HDR_WORDS] = {};
   // Plans alternate between two halves of the int workspace, each with a
@@ -199,7 +200,8 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
       const pod_plan_desc& f = ctx->policy;
       bool same = d.num_qo_heads == f.num_qo_heads && d.num_kv_heads == f.num_kv_heads &&
                   d.head_dim == f.head_dim && d.page_size == f.page_size && d.dtype == f.dtype &&
-                  (d.has_sinks != 0) == (f.has_sinks != 0) && d.num_cus == f.num_cus;
+                  (d.has_sinks != 0) == (f.has_sinks != 0) && d.num_cus == f.num_cus &&
+                  d.decode_kv_dtype == f.decode_kv_dtype;
       const pod_role_desc* a[2] = {&d.prefill, &d.decode};
       const pod_role_desc* b[2] = {&f.prefill, &f.decode};
       for (int r = 0; r < 2; ++r)
@@ -207,8 +209,9 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
                a[r]->window_left == b[r]->window_left && a[r]->sm_scale == b[r]->sm_scale;
       if (!same)
         return set_err(POD_ERR_INVALID,
-                       "graph context: heads, head_dim, page_size, dtype, sinks, num_cus and each "
-                       "role's causal / window_left / sm_scale must stay those of the first plan");
+                       "graph context: heads, head_dim, page_size, dtype, decode_kv_dtype, sinks, "
+                       "num_cus and each role's causal / window_left / sm_scale must stay those of "
+                       "the first plan");
     }
   }
   DeviceGuard dg(ctx->device);
@@ -309,6 +312,7 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   ctx->page_size = d.page_size;
   ctx->dtype = d.dtype;
   ctx->has_sinks = d.has_sinks ? 1 : 0;
+  ctx->decode_kv_fp8 = d.decode_kv_dtype == POD_DTYPE_FP8_E4M3;
   ctx->info = inf;
   memcpy(ctx->hdr, ctx->staging[k], sizeof(ctx->hdr));
   ctx->planned = true;
@@ -338,6 +342,8 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     const RolePlan& rp = ctx->role[r];
     const pod_role_args& a = *ra[r];
     pod::RoleParams& o = p.role[r];
+    const bool fp8 = r == 1 && ctx->decode_kv_fp8;
+    const int esz = fp8 ? 1 : 2;   // bytes per K/V element
     if (rp.rows > 0) {
       if (!a.q || !a.k_cache || !a.v_cache || !a.out)
         return set_err(POD_ERR_INVALID, std::string(names[r]) + ": q, k_cache, v_cache and out are required");
@@ -352,6 +358,10 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
       if ((mis & 15) || (smis & 7))
         return set_err(POD_ERR_INVALID, std::string(names[r]) +
                                              ": buffers must be 16-byte aligned and strides multiples of 8 elements");
+      if (fp8 && ((a.kv_stride_page | a.kv_stride_tok | a.kv_stride_head) & 15))
+        return set_err(POD_ERR_INVALID, "decode: FP8 K/V strides must be multiples of 16 elements");
+      if (fp8 && !a.kv_indices)
+        return set_err(POD_ERR_INVALID, "decode: FP8 K/V needs kv_indices (no identity page table)");
       const int64_t lim = (int64_t)1 << 30;   // bytes = 2 * elements must stay below 2^31
       if (a.kv_stride_page >= lim || a.kv_stride_tok >= lim || a.kv_stride_head >= lim)
         return set_err(POD_ERR_UNSUPPORTED, std::string(names[r]) +
@@ -364,15 +374,21 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     o.q_sh = a.q_stride_head;
     o.k = a.k_cache;
     o.v = a.v_cache;
-    o.kv_sp_b = (uint32_t)(a.kv_stride_page * 2);
-    o.kv_st_b = (uint32_t)(a.kv_stride_tok * 2);
-    o.kv_sh_b = (uint32_t)(a.kv_stride_head * 2);
+    o.kv_sp_b = (uint32_t)(a.kv_stride_page * esz);
+    o.kv_st_b = (uint32_t)(a.kv_stride_tok * esz);
+    o.kv_sh_b = (uint32_t)(a.kv_stride_head * esz);
+    o.kv_fp8 = fp8 ? 1 : 0;
     o.indices = a.kv_indices;
     o.out = a.out;
     o.o_st = a.out_stride_tok;
     o.o_sh = a.out_stride_head;
     o.lse = a.lse;
-    o.scale_log2 = rp.sm_scale * 1.4426950408889634f;
+    // the decode role's FP8 calibration: q_scale * k_scale fold into the scale,
+    // v_scale into the output normalisation (0 = 1)
+    const auto one = [](float s) { return s == 0.f ? 1.f : s; };
+    const float qk = r == 1 ? one(args->q_scale_d) * one(args->k_scale_d) : 1.f;
+    o.scale_log2 = rp.sm_scale * qk * 1.4426950408889634f;
+    o.v_scale = r == 1 ? one(args->v_scale_d) : 1.f;
     o.causal = rp.causal;
     o.window_left = rp.window_left;
   }

@@ -61,9 +61,11 @@ struct RoleParams {
   void* out;
   int64_t o_st, o_sh;
   float* lse;               // nullptr = not requested
-  float scale_log2;         // sm_scale * log2(e)
+  float scale_log2;         // sm_scale * q_scale * k_scale * log2(e)
+  float v_scale;            // output factor (the decode role's FP8 v_scale; else 1)
   int32_t causal;
   int32_t window_left;
+  int32_t kv_fp8;           // K/V pools hold FP8 E4M3 (key-chunk items only)
 };
 
 struct Params {

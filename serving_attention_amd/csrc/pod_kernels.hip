@@ -36,6 +36,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "pod_internal.h"
 
 namespace pod {
@@ -225,6 +227,7 @@ struct RoleView {
   int64_t o_st, o_sh;
   float* lse;
   float scale_log2;
+  float v_scale;            // output factor (FP8 calibration; 1 otherwise)
   int causal, window_left;
 };
 
@@ -258,6 +261,7 @@ __device__ __forceinline__ RoleView pick_role(PArg p, int role, int kvh) {
   r.o_sh = role ? b.o_sh : a.o_sh;
   r.lse = role ? b.lse : a.lse;
   r.scale_log2 = role ? b.scale_log2 : a.scale_log2;
+  r.v_scale = role ? b.v_scale : a.v_scale;
   r.causal = role ? b.causal : a.causal;
   r.window_left = role ? b.window_left : a.window_left;
   return r;
@@ -396,7 +400,7 @@ __device__ __forceinline__ TileDesc tile_desc(CI32* tdesc, int idx) {
 
 
 template <typename T, bool kPow2>
-__device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt, const int32_t* tab,
+__device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt, const int32_t* tab,
                             int nv, char* ring, char* idring, float* sink_lds, char* pf_lds) {
   using V8 = typename Dt<T>::v8;
   CI32* ctab = plan_words(tab);
@@ -572,7 +576,7 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
     const float mu2 = m * sl2;
     float den = lt;
     if (q.sinks) den += fast_exp2(sink_lds[head] * kLog2e - mu2);
-    const float inv = den > 0.f ? 1.f / den : 0.f;
+    const float inv = den > 0.f ? r.v_scale / den : 0.f;
     // Output accumulator j = 4a + c of lane half hi is d = db*32 + 8a + 4hi + c.
     // Per pair a = 2b, 2b+1 one swap between the lane halves (all lanes take
     // part) leaves each half 8 consecutive d: the lower half d = 16b + [0, 8),
@@ -908,6 +912,25 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
   finish(cur);
 }
 
+// Sixteen FP8 E4M3 values (one 16-byte load) widened exactly to T: the two
+// 16-byte chunks of 8 values each (values 0-7, then 8-15).
+template <typename T>
+__device__ __forceinline__ void fp8x16_widen(const u32x4 w, u32x4& c0, u32x4& c1) {
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (std::is_same<T, __bf16>::value) {
+      o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, false));
+      o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], 1.0f, true));
+    } else {
+      o[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, false));
+      o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[i], 1.0f, true));
+    }
+  }
+  c0 = u32x4{o[0], o[1], o[2], o[3]};
+  c1 = u32x4{o[4], o[5], o[6], o[7]};
+}
+
 // ----------------------------------------------------------------------------
 // Key chunk: all q_len x group rows (<= 32) of one request and kv head over keys
 // [kv_begin, kv_end). Wave w takes 32-key steps w, w+8, ... Each wave load
@@ -916,7 +939,7 @@ __device__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt
 // read. The next step's rows are in flight while the current step computes,
 // and the page indices are fetched one step further ahead.
 // Wave states merge in LDS; split chunks merge through the float workspace.
-template <typename T>
+template <typename T, bool kFp8>
 __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowGeom& rg, int kvh,
                            int kv_begin, int kv_end, int split, int grp, char* lds) {
   using V8 = typename Dt<T>::v8;
@@ -954,47 +977,10 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
   for (int c = 0; c < 8; ++c) koff[c] = krow * kRowBytes + (((hi * 8 + c) ^ swz(krow)) << 4);
   const char* vlane = Vw + vt_lane(lane);
 
-  // loads: instruction i moves row 4 i + (lane >> 4) of the step, slot lane & 15
-  const int ld_row = lane >> 4, ld_slot = lane & 15;
   const int first = kv_begin + kStepKeys * wave;
   const int n_steps = first < kv_end ? (kv_end - first + kWaves * kStepKeys - 1) / (kWaves * kStepKeys) : 0;
-  uint32_t pidx[8];
-  u32x4 kst[8], vst[8];
-  auto load_pages = [&](int i) {
-    const int kb = first + kWaves * kStepKeys * i;
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      pidx[c] = page_of(r, p, rg.page_start, min(kb + 4 * c + ld_row, kv_end - 1));
-  };
-  // rows past kv_end repeat row kv_end - 1 (masked to zero weight)
-  auto load_rows = [&](int i) {
-    const int kb = first + kWaves * kStepKeys * i;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint64_t off = row_off(r, p, pidx[c], min(kb + 4 * c + ld_row, kv_end - 1));
-      kst[c] = ld16(r.k + off + ((ld_slot ^ swz(4 * c + ld_row)) << 4));
-      vst[c] = ld16(r.v + off + (ld_slot << 4));
-    }
-  };
-
-  if (n_steps > 0) {
-    load_pages(0);
-    load_rows(0);
-    if (n_steps > 1) load_pages(1);
-  }
-  for (int i = 0; i < n_steps; ++i) {
-    const int kb = first + kWaves * kStepKeys * i;
-    // this step's rows to the wave's blocks; the previous step's reads of them
-    // are ordered before these writes (LDS runs a wave's requests in order)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      lds_st16(Kw, (4 * c + ld_row) * kRowBytes + (ld_slot << 4), kst[c]);
-      lds_st16(Vw, (4 * c + ld_row) * kVRowBytes + (ld_slot << 4), vst[c]);
-    }
-    if (i + 1 < n_steps) {
-      load_rows(i + 1);
-      if (i + 2 < n_steps) load_pages(i + 2);
-    }
+  // one step's scores, softmax and P.V from the wave's LDS blocks (keys kb..)
+  auto compute = [&](int kb) __attribute__((always_inline)) {
     f32x16 s[1];
     s[0] = f32x16{};
 #pragma unroll
@@ -1014,6 +1000,112 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
 #pragma unroll
       for (int db = 0; db < 4; ++db)
         o[db] = Dt<T>::mfma(vt_operand<V8>(vlane, 16 * mp, db * 32), pb[0][mp], o[db]);
+  };
+  auto step_kb = [&](int i) { return first + kWaves * kStepKeys * i; };
+
+  if constexpr (!kFp8) {
+    // loads: instruction c moves row 4c + (lane >> 4) of the step, slot lane & 15
+    const int ld_row = lane >> 4, ld_slot = lane & 15;
+    uint32_t pidx[8];
+    u32x4 kst[8], vst[8];
+    auto load_pages = [&](int i) {
+      const int kb = step_kb(i);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        pidx[c] = page_of(r, p, rg.page_start, min(kb + 4 * c + ld_row, kv_end - 1));
+    };
+    // rows past kv_end repeat row kv_end - 1 (masked to zero weight)
+    auto load_rows = [&](int i) {
+      const int kb = step_kb(i);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const uint64_t off = row_off(r, p, pidx[c], min(kb + 4 * c + ld_row, kv_end - 1));
+        kst[c] = ld16(r.k + off + ((ld_slot ^ swz(4 * c + ld_row)) << 4));
+        vst[c] = ld16(r.v + off + (ld_slot << 4));
+      }
+    };
+    if (n_steps > 0) {
+      load_pages(0);
+      load_rows(0);
+      if (n_steps > 1) load_pages(1);
+    }
+    for (int i = 0; i < n_steps; ++i) {
+      // this step's rows to the wave's blocks; the previous step's reads of them
+      // are ordered before these writes (LDS runs a wave's requests in order)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        lds_st16(Kw, (4 * c + ld_row) * kRowBytes + (ld_slot << 4), kst[c]);
+        lds_st16(Vw, (4 * c + ld_row) * kVRowBytes + (ld_slot << 4), vst[c]);
+      }
+      if (i + 1 < n_steps) {
+        load_rows(i + 1);
+        if (i + 2 < n_steps) load_pages(i + 2);
+      }
+      compute(step_kb(i));
+    }
+  } else {
+    // FP8 rows are 128 bytes: instruction c moves row 8c + (lane >> 3) of the
+    // step, bytes 16 (lane & 7) .. +16, widened to two 16-byte chunks of T in the
+    // same LDS layout. A step is half the bytes, so two steps stay in flight
+    // (register sets a and b, steps alternating), page ids two steps ahead.
+    // Every load here is unconditional, so the compiler can count the ones in
+    // flight (a load under a branch, or a register a load targets being
+    // overwritten on one path, makes it wait for all of them): FP8 pools always
+    // come with a page table, and loads past the chunk repeat its last row
+    // (cache hits, never computed on).
+    const int ld_row = lane >> 3, ld_part = lane & 7;
+    const int32_t* const id_base = r.indices + rg.page_start;
+    uint32_t pa[4], pb2[4];
+    u32x4 ka[4], va[4], kb2[4], vb2[4];
+    auto load_pages = [&](int i, uint32_t (&pi)[4]) {
+      const int kb = step_kb(i);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int key = min(kb + 8 * c + ld_row, kv_end - 1);
+        const int pg = p.page_shift >= 0 ? (key >> p.page_shift) : key / p.page_size;
+        pi[c] = (uint32_t)id_base[pg];
+      }
+    };
+    auto load_rows = [&](int i, const uint32_t (&pi)[4], u32x4 (&kk)[4], u32x4 (&vv)[4]) {
+      const int kb = step_kb(i);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint64_t off = row_off(r, p, pi[c], min(kb + 8 * c + ld_row, kv_end - 1)) + (ld_part << 4);
+        kk[c] = ld16(r.k + off);
+        vv[c] = ld16(r.v + off);
+      }
+    };
+    auto store_rows = [&](const u32x4 (&kk)[4], const u32x4 (&vv)[4]) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int row = 8 * c + ld_row;
+        u32x4 k0, k1, v0, v1;
+        fp8x16_widen<T>(kk[c], k0, k1);
+        fp8x16_widen<T>(vv[c], v0, v1);
+        lds_st16(Kw, row * kRowBytes + (((2 * ld_part) ^ swz(row)) << 4), k0);
+        lds_st16(Kw, row * kRowBytes + (((2 * ld_part + 1) ^ swz(row)) << 4), k1);
+        lds_st16(Vw, row * kVRowBytes + ((2 * ld_part) << 4), v0);
+        lds_st16(Vw, row * kVRowBytes + ((2 * ld_part + 1) << 4), v1);
+      }
+    };
+    if (n_steps > 0) {
+      load_pages(0, pa);
+      load_rows(0, pa, ka, va);
+      load_pages(1, pb2);
+      load_rows(1, pb2, kb2, vb2);
+      load_pages(2, pa);
+      load_pages(3, pb2);
+      for (int i = 0; i < n_steps; i += 2) {
+        store_rows(ka, va);
+        load_rows(i + 2, pa, ka, va);
+        load_pages(i + 4, pa);
+        compute(step_kb(i));
+        store_rows(kb2, vb2);
+        load_rows(i + 3, pb2, kb2, vb2);
+        load_pages(i + 5, pb2);
+        if (i + 1 < n_steps) compute(step_kb(i + 1));
+      }
+    }
   }
   l = xhalf_sum(l);
 
@@ -1077,7 +1169,7 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
       const float mu = (Mr == kNegInf) ? 0.f : Mr;
       float den = L;
       if (p.sinks) den += fast_exp2(sink_l2 - mu);
-      const float inv = den > 0.f ? 1.f / den : 0.f;
+      const float inv = den > 0.f ? r.v_scale / den : 0.f;
       V8 w0, w1;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -1142,7 +1234,7 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
       }
     }
     const float L = tot > 0.f ? Mx + fast_log2(tot) : kNegInf;
-    float inv = tot > 0.f ? 1.f / tot : 0.f;
+    float inv = tot > 0.f ? r.v_scale / tot : 0.f;
     if (p.sinks && tot > 0.f) inv = inv / (1.f + fast_exp2(sink_l2 - L));
     V8 w0, w1;
 #pragma unroll
@@ -1186,7 +1278,10 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
     const RoleView r = pick_role(p, flags & kFlagRole, kvh);
     CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
     const RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
-    chunk_item<T>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds);
+    if ((flags & kFlagRole) && p.role[1].kv_fp8)
+      chunk_item<T, true>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds);
+    else
+      chunk_item<T, false>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds);
   };
   auto run_chunks = [&]() {
     for (int j = 0; j < n_chunks; ++j) {

@@ -131,8 +131,14 @@ class BatchPOD:
              dtype=torch.bfloat16, causal_p: bool = True, causal_d: bool = True,
              window_left_p: int = -1, window_left_d: int = -1,
              sm_scale_p: Optional[float] = None, sm_scale_d: Optional[float] = None,
-             sinks: bool = False, decode_chunk: int = 0, order: int = 0, stream=None):
-        """Build and upload the work list. Either role may be None (empty)."""
+             sinks: bool = False, decode_chunk: int = 0, order: int = 0, stream=None,
+             kv_dtype_d=None):
+        """Build and upload the work list. Either role may be None (empty).
+
+        ``kv_dtype_d=torch.float8_e4m3fn`` plans the decode role over an FP8 KV
+        cache (POD article, "Prefill 侧参数": the calibration scales are decode
+        run parameters); q and outputs keep ``dtype``.
+        """
         keep = []
         desc = _lib.PodPlanDesc(
             self._role_desc(qo_indptr_p, kv_indptr_p, last_page_len_p, causal_p, window_left_p,
@@ -140,7 +146,10 @@ class BatchPOD:
             self._role_desc(qo_indptr_d, kv_indptr_d, last_page_len_d, causal_d, window_left_d,
                             sm_scale_d, keep),
             int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size),
-            _dtype_code(dtype), int(bool(sinks)), 0, int(decode_chunk), int(order))
+            _dtype_code(dtype), int(bool(sinks)), 0, int(decode_chunk), int(order),
+            _lib.POD_DTYPE_FP8_E4M3 if kv_dtype_d == torch.float8_e4m3fn else 0)
+        if kv_dtype_d not in (None, torch.float8_e4m3fn) and _DT.get(kv_dtype_d) != _dtype_code(dtype):
+            raise NotImplementedError(f"decode K/V dtype {kv_dtype_d} is not supported")
         s = _stream_handle(self.device) if stream is None else ctypes.c_void_p(stream)
         _lib.check(self._lib.pod_plan(self._ctx, ctypes.byref(desc), s))
         nnz = []
@@ -152,7 +161,7 @@ class BatchPOD:
             rows=tuple(rows), nnz=tuple(nnz),
             num_qo_heads=int(num_qo_heads), num_kv_heads=int(num_kv_heads),
             head_dim=int(head_dim), page_size=int(page_size), dtype=_dtype_code(dtype),
-            sinks=bool(sinks))
+            sinks=bool(sinks), fp8_d=kv_dtype_d == torch.float8_e4m3fn)
         return self
 
     def plan_info(self) -> dict:
@@ -175,8 +184,9 @@ class BatchPOD:
         if q.stride(-1) != 1:
             raise ValueError("q: head_dim must be dense")
         k, v, sp, st, sh = kv_views(cache, self.kv_layout)
-        if k.dtype != q.dtype:
-            raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "kv dtype differs from q dtype")
+        want = torch.float8_e4m3fn if (idx == 1 and pl["fp8_d"]) else q.dtype
+        if k.dtype != want:
+            raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, f"kv dtype {k.dtype} differs from the planned {want}")
         ps = k.shape[1] if self.kv_layout == "NHD" else k.shape[2]
         hk = k.shape[2] if self.kv_layout == "NHD" else k.shape[1]
         if ps != pl["page_size"] or hk != pl["num_kv_heads"] or k.shape[3] != d:
@@ -197,8 +207,15 @@ class BatchPOD:
 
     def run(self, q_p, paged_kv_cache_p, kv_indices_p, q_d, paged_kv_cache_d, kv_indices_d, *,
             sinks: Optional[torch.Tensor] = None, return_lse: bool = False,
-            out_p=None, out_d=None, lse_p=None, lse_d=None):
-        """One fused launch. Returns (out_p, out_d) or ((out_p, lse_p), (out_d, lse_d))."""
+            out_p=None, out_d=None, lse_p=None, lse_d=None,
+            q_scale_d: Optional[float] = None, k_scale_d: Optional[float] = None,
+            v_scale_d: Optional[float] = None):
+        """One fused launch. Returns (out_p, out_d) or ((out_p, lse_p), (out_d, lse_d)).
+
+        q_scale_d * k_scale_d multiply the decode sm_scale and v_scale_d the decode
+        output (POD article, "Prefill 侧参数"; here v_scale is folded into the
+        launch's final normalisation). None means 1.
+        """
         if self._planned is None:
             raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "run() before plan()")
         pl = self._planned
@@ -227,7 +244,8 @@ class BatchPOD:
         args = _lib.PodRunArgs(
             self._role_args(0, q_p, paged_kv_cache_p, kv_indices_p, outs[0], lses[0]),
             self._role_args(1, q_d, paged_kv_cache_d, kv_indices_d, outs[1], lses[1]),
-            sinks.data_ptr() if sinks is not None else None)
+            sinks.data_ptr() if sinks is not None else None,
+            float(q_scale_d or 0.0), float(k_scale_d or 0.0), float(v_scale_d or 0.0))
         _lib.check(self._lib.pod_run(self._ctx, ctypes.byref(args), _stream_handle(self.device)))
         if return_lse:
             return (outs[0], lses[0]), (outs[1], lses[1])

@@ -35,7 +35,8 @@ def plan_and_run(w, roles=("prefill", "decode"), decode_chunk=0, order=0, ws_mb=
              causal_p=p.causal if p else True, causal_d=d.causal if d else True,
              window_left_p=p.window_left if p else -1, window_left_d=d.window_left if d else -1,
              sm_scale_p=p.sm_scale if p else None, sm_scale_d=d.sm_scale if d else None,
-             sinks=spec.sinks, decode_chunk=decode_chunk, order=order)
+             sinks=spec.sinks, decode_chunk=decode_chunk, order=order,
+             kv_dtype_d=torch.float8_e4m3fn if spec.decode_kv_dtype == "fp8_e4m3" else None)
     outs = {}
     for name, r in (("p", p), ("d", d)):
         if r is None:
@@ -51,9 +52,17 @@ def plan_and_run(w, roles=("prefill", "decode"), decode_chunk=0, order=0, ws_mb=
                   d.q if d else None, d.kv_cache if d else None, d.kv_indices_dev if d else None,
                   sinks=w.sinks if spec.sinks else None, return_lse=return_lse,
                   out_p=outs["p"][0], out_d=outs["d"][0],
-                  lse_p=outs["p"][1] if return_lse else None, lse_d=outs["d"][1] if return_lse else None)
+                  lse_p=outs["p"][1] if return_lse else None, lse_d=outs["d"][1] if return_lse else None,
+                  **fp8_scale_args(spec))
     torch.cuda.synchronize()
     return res, pod
+
+
+def fp8_scale_args(spec):
+    if spec.decode_kv_dtype != "fp8_e4m3":
+        return {}
+    qs, ks, vs = spec.fp8_scales
+    return dict(q_scale_d=qs, k_scale_d=ks, v_scale_d=vs)
 
 
 def oracle_request(w, role, b, rows=None):
@@ -64,17 +73,26 @@ def oracle_request(w, role, b, rows=None):
     spec = w.spec
     p0, p1 = int(role.kv_indptr[b]), int(role.kv_indptr[b + 1])
     pages = torch.from_numpy(role.kv_indices[p0:p1].astype(np.int64)).to(role.k_pool.device)
-    kp = role.k_pool.index_select(0, pages).float().cpu().numpy()
-    vp = role.v_pool.index_select(0, pages).float().cpu().numpy()
+    fp8 = role is w.decode and spec.decode_kv_dtype == "fp8_e4m3"
+    qs, ks, vs = spec.fp8_scales if fp8 else (1.0, 1.0, 1.0)
+    if fp8:   # the oracle's own E4M3 decoding of the stored bytes
+        kp = oracle.e4m3_to_float(role.k_pool.view(torch.uint8).index_select(0, pages).cpu().numpy())
+        vp = oracle.e4m3_to_float(role.v_pool.view(torch.uint8).index_select(0, pages).cpu().numpy())
+    else:
+        kp = role.k_pool.index_select(0, pages).float().cpu().numpy()
+        vp = role.v_pool.index_select(0, pages).float().cpu().numpy()
     q0, q1 = int(role.qo_indptr[b]), int(role.qo_indptr[b + 1])
     q = role.q[q0:q1].float().cpu().numpy()
     sinks = w.sinks.cpu().numpy() if spec.sinks else None
     res = oracle.attend_role(
         q, kp, vp, np.array([0, q1 - q0]), np.array([0, p1 - p0]), None,
         role.last_page_len[b:b + 1], spec.page_size, spec.num_qo_heads, spec.num_kv_heads,
-        role.causal, role.window_left, role.sm_scale, sinks, layout=spec.kv_layout,
+        role.causal, role.window_left, role.sm_scale * qs * ks, sinks, layout=spec.kv_layout,
         rows_of=(lambda _: rows) if rows is not None else None)
-    return res[0]
+    ids, ro, rl = res[0]
+    # attend_rows_fp8_scaled's definition: q_scale * k_scale on the scores,
+    # v_scale on the output
+    return ids, ro * vs, rl
 
 
 def compare_role(w, role, out, lse, requests=None, rows_of=None, tag=""):

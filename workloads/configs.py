@@ -63,6 +63,10 @@ class WorkloadSpec:
     sm_scale: Optional[float] = None
     meta_seed: int = 0
     value_seed: int = 1000
+    # FP8 E4M3 decode K/V ("fp8_e4m3"; needs separate pools) and the decode
+    # role's calibration scales (q_scale, k_scale, v_scale) of the POD article
+    decode_kv_dtype: Optional[str] = None
+    fp8_scales: tuple = (1.0, 1.0, 1.0)
 
 
 @dataclass
@@ -159,6 +163,14 @@ def named_spec(name: str) -> WorkloadSpec:
             decode=RoleSpec(qo_lens=[1] * 128, kv_lens=[2048] * 128, causal=True),
             num_qo_heads=64, num_kv_heads=8, page_size=1, dtype="bf16",
             sm_scale=scale, meta_seed=4, value_seed=1004)
+    if name == "pod_fp8":
+        # the pod workload with the decode role over an FP8 E4M3 KV cache and
+        # calibration scales (q, k, v) of the POD article's decode parameters
+        s = named_spec("pod")
+        s.name = name
+        s.decode_kv_dtype = "fp8_e4m3"
+        s.fp8_scales = (1.0, 0.75, 1.25)
+        return s
     if name == "pod_chunked":
         # 4096-token prefill chunk on a 16384-token prefix plus 256 four-token decodes.
         rng = np.random.default_rng(5)
@@ -172,7 +184,7 @@ def named_spec(name: str) -> WorkloadSpec:
     raise KeyError(name)
 
 
-NAMED = ("single_decode", "batch_decode", "batch_prefill", "pod", "pod_chunked")
+NAMED = ("single_decode", "batch_decode", "batch_prefill", "pod", "pod_chunked", "pod_fp8")
 
 
 def _role_pages(role: RoleSpec, ps: int):
@@ -214,15 +226,18 @@ def build(spec: WorkloadSpec, device="cpu", poison: bool = False) -> Workload:
     gen = torch.Generator(device=device)
     gen.manual_seed(spec.value_seed)
 
-    def alloc_pool(npages):
+    def alloc_pool(npages, tdt):
         shape = (npages, 2, ps, hkv, d) if spec.kv_layout == "NHD" else (npages, 2, hkv, ps, d)
-        t = torch.empty(shape, dtype=dt, device=device)
+        t = torch.empty(shape, dtype=tdt, device=device)
         _fill_randn_(t, gen)
         return t
 
+    assert spec.decode_kv_dtype in (None, "fp8_e4m3")
+    assert spec.decode_kv_dtype is None or spec.pool == "separate", "FP8 decode K/V needs its own pool"
     pools = {}
     for key in pool_sizes:
-        pools[key] = alloc_pool(pool_sizes[key])
+        fp8 = key == "decode" and spec.decode_kv_dtype == "fp8_e4m3"
+        pools[key] = alloc_pool(pool_sizes[key], torch.float8_e4m3fn if fp8 else dt)
 
     out = {}
     logical_base = 0
