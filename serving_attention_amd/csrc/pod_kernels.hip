@@ -941,11 +941,13 @@ __device__ __forceinline__ void fp8x16_widen(const u32x4 w, u32x4& c0, u32x4& c1
 // Wave states merge in LDS; split chunks merge through the float workspace.
 template <typename T, bool kFp8>
 __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowGeom& rg, int kvh,
-                           int kv_begin, int kv_end, int split, int grp, char* lds) {
+                           int kv_begin, int kv_end, int split, int grp, char* lds, int wave_s) {
   using V8 = typename Dt<T>::v8;
-  // the thread index, opaque to the compiler so that nothing derived from it
-  // is computed once for all items of the workgroup and held in registers
-  int tid = threadIdx.x;
+  // the thread index, rebuilt from the wave (scalar) and the lane count, so the
+  // hardware's thread-id register need not live through the whole launch; and
+  // opaque to the compiler, so nothing derived from it is computed once for
+  // all items of the workgroup and held in registers
+  int tid = wave_s * 64 + (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
@@ -1216,21 +1218,39 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
   auto ld_c = [](const float* a) { return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); };
   if (fok) {
     const float* base = p.partials + (int64_t)first_slot * kSlotFloats;
+    // the partials' loads go out in batches (8 LSEs, then 4 states of 17 words),
+    // so a merge of many splits waits for a few memory round trips, not one per
+    // split; indices past the last split re-read it and weigh nothing
+    const float* lse_col = base + kChunkRows * kHeadDim + frow;
     float Mx = kNegInf;
-    for (int s = 0; s < n_splits; ++s)
-      Mx = fmaxf(Mx, ld_c(base + (int64_t)s * kSlotFloats + kChunkRows * kHeadDim + frow));
+    for (int s = 0; s < n_splits; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = ld_c(lse_col + (int64_t)min(s + u, n_splits - 1) * kSlotFloats);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) Mx = fmaxf(Mx, v[u]);
+    }
     float acc16[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc16[i] = 0.f;
     float tot = 0.f;
     if (Mx != kNegInf) {
-      for (int s = 0; s < n_splits; ++s) {
-        const float* sl = base + (int64_t)s * kSlotFloats;
-        const float w = fast_exp2(ld_c(sl + kChunkRows * kHeadDim + frow) - Mx);
-        tot += w;
-        const float* src = sl + frow * kHeadDim + d0;
+      for (int s = 0; s < n_splits; s += 4) {
+        float lv[4], x[4][16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc16[i] += w * ld_c(src + i);
+        for (int u = 0; u < 4; ++u) {
+          const float* sl = base + (int64_t)min(s + u, n_splits - 1) * kSlotFloats;
+          lv[u] = ld_c(sl + kChunkRows * kHeadDim + frow);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) x[u][i] = ld_c(sl + frow * kHeadDim + d0 + i);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = s + u < n_splits ? fast_exp2(lv[u] - Mx) : 0.f;
+          tot += w;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc16[i] += w * x[u][i];
+        }
       }
     }
     const float L = tot > 0.f ? Mx + fast_log2(tot) : kNegInf;
@@ -1267,6 +1287,7 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
   __shared__ int pool_slot;
   // destination of the block-table prefetch
   __shared__ __attribute__((aligned(16))) char pf_lds[256];
+  const int wave_s = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   CI32* wg = plan_words(image_region(p, kHdrWgs)) + blockIdx.x * kWgWords;
   const int first_item = wg[0], n_tiles = wg[1], n_chunks = wg[2];
   const int first_blk = wg[3], n_blk = wg[4];
@@ -1279,9 +1300,9 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
     CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
     const RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
     if ((flags & kFlagRole) && p.role[1].kv_fp8)
-      chunk_item<T, true>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds);
+      chunk_item<T, true>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
     else
-      chunk_item<T, false>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds);
+      chunk_item<T, false>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
   };
   auto run_chunks = [&]() {
     for (int j = 0; j < n_chunks; ++j) {
