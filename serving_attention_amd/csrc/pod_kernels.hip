@@ -1091,11 +1091,14 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
       }
     };
     if (n_steps > 0) {
+      // the prologue leaves the loads in flight in the loop's own order (rows
+      // of a step, then the page ids two steps on), so the compiler's count of
+      // them at the loop head is exact
       load_pages(0, pa);
-      load_rows(0, pa, ka, va);
       load_pages(1, pb2);
-      load_rows(1, pb2, kb2, vb2);
+      load_rows(0, pa, ka, va);
       load_pages(2, pa);
+      load_rows(1, pb2, kb2, vb2);
       load_pages(3, pb2);
       for (int i = 0; i < n_steps; i += 2) {
         store_rows(ka, va);
