@@ -47,6 +47,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -65,6 +66,9 @@ struct Dt<__bf16> {
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
 };
 template <>
 struct Dt<_Float16> {
@@ -72,6 +76,9 @@ struct Dt<_Float16> {
   using v4 = f16x4;
   static __device__ __forceinline__ f32x16 mfma(v8 a, v8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mfma16(v8 a, v8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
 };
 
@@ -939,7 +946,14 @@ __device__ __forceinline__ void fp8x16_widen(const u32x4 w, u32x4& c0, u32x4& c1
 // read. The next step's rows are in flight while the current step computes,
 // and the page indices are fetched one step further ahead.
 // Wave states merge in LDS; split chunks merge through the float workspace.
-template <typename T, bool kFp8>
+// kCols 32: the rows are one 32-wide MFMA column block (32x32x16 MFMAs).
+// kCols 16: at most 16 rows; 16x16x32 MFMAs, half the MFMA and softmax work per
+// key. Score block b (16 keys) holds key 16b + 4(lane/16) + j in accumulator j of
+// column lane % 16; the 8 keys of a lane, in that order, are also the k-slots of
+// its P^T operand (slot 8(lane/16) + e), so the V^T operand reads keys 4(lane/16)
+// + [0,4) and 16 + 4(lane/16) + [0,4); head dims go to lane group q = lane/16 as
+// d = 32q + 8c + [0,8) in the c-th score MFMA.
+template <typename T, bool kFp8, int kCols>
 __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowGeom& rg, int kvh,
                            int kv_begin, int kv_end, int split, int grp, char* lds, int wave_s) {
   using V8 = typename Dt<T>::v8;
@@ -951,14 +965,23 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, hi = lane >> 5;
+  const int q16 = lane >> 4;                       // 16-column mode: lane group
+  const int col = kCols == 16 ? (lane & 15) : r32;   // this lane's row of the item
   const int g = p.group_size;
   const int rows = rg.qo_len * g;
-  const bool row_ok = r32 < rows;
-  const int tok = row_ok ? r32 / g : 0;
-  const int head = kvh * g + (row_ok ? r32 % g : 0);
+  const bool row_ok = col < rows;
+  const int tok = row_ok ? col / g : 0;
+  const int head = kvh * g + (row_ok ? col % g : 0);
 
   V8 qreg[8];
-  load_q<T>(qreg, r, row_ok, rg.qo_start + tok, head, hi);
+  if constexpr (kCols == 32) {
+    load_q<T>(qreg, r, row_ok, rg.qo_start + tok, head, hi);
+  } else {
+    const T* qp = reinterpret_cast<const T*>(r.q) + (int64_t)(rg.qo_start + tok) * r.q_st +
+                  (int64_t)head * r.q_sh + 32 * q16;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qreg[c] = __builtin_bit_cast(V8, row_ok ? ld16(qp + 8 * c) : u32x4{0, 0, 0, 0});
+  }
 
   const int pdiag = rg.kv_len - rg.qo_len + tok;
   const int key_hi = min(r.causal ? pdiag : rg.kv_len - 1, kv_end - 1);
@@ -968,21 +991,96 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
   char* Kw = lds + wave * kWaveLds;
   char* Vw = Kw + kWaveKBytes;
   f32x16 o[4];
+  f32x4 o16[8];
 #pragma unroll
   for (int b = 0; b < 4; ++b) o[b] = f32x16{};
+#pragma unroll
+  for (int b = 0; b < 8; ++b) o16[b] = f32x4{};
   float m = kNegInf, l = 0.f;
   const float sl2 = r.scale_log2;
 
-  const int krow = key_row(r32);
+  // K operand offsets: 32 columns, MFMA c reads chunk 8 hi + c of row key_row(r32);
+  // 16 columns, block b and MFMA c read chunk 4 q16 + c of row 16 b + lane % 16
   int koff[8];
+  const char* vlane;
+  if constexpr (kCols == 32) {
+    const int krow = key_row(r32);
 #pragma unroll
-  for (int c = 0; c < 8; ++c) koff[c] = krow * kRowBytes + (((hi * 8 + c) ^ swz(krow)) << 4);
-  const char* vlane = Vw + vt_lane(lane);
+    for (int c = 0; c < 8; ++c) koff[c] = krow * kRowBytes + (((hi * 8 + c) ^ swz(krow)) << 4);
+    vlane = Vw + vt_lane(lane);
+  } else {
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int row = 16 * b + (lane & 15);
+        koff[4 * b + c] = row * kRowBytes + (((4 * q16 + c) ^ swz(row)) << 4);
+      }
+    // V^T: lane i of group q addresses row 4q + i/4, dims 4(i%4) (+ block offset)
+    vlane = Vw + (4 * q16 + ((lane & 15) >> 2)) * kVRowBytes + 8 * (lane & 3);
+  }
 
   const int first = kv_begin + kStepKeys * wave;
   const int n_steps = first < kv_end ? (kv_end - first + kWaves * kStepKeys - 1) / (kWaves * kStepKeys) : 0;
   // one step's scores, softmax and P.V from the wave's LDS blocks (keys kb..)
+  auto compute16 = [&](int kb) __attribute__((always_inline)) {
+    f32x4 s[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      s[b] = f32x4{};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        s[b] = Dt<T>::mfma16(__builtin_bit_cast(V8, lds_ld16(Kw, koff[4 * b + c])), qreg[c], s[b]);
+    }
+    const int kq = kb + 4 * q16;
+    if (__any((unsigned)(kb - rm.lo) > rm.span || (unsigned)(kb + kStepKeys - 1 - rm.lo) > rm.span)) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          s[b][j] = ((unsigned)(kq + 16 * b + j - rm.lo) <= rm.span) ? s[b][j] : kNegInf;
+    }
+    // column max over the lane's 8 keys and the other three lane groups
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool upd = (m == kNegInf) ? (mx != kNegInf) : ((mx - m) * sl2 > kRescaleThreshold);
+    if (__any(upd)) {
+      const float mn = upd ? mx : m;
+      const float alpha = upd ? fast_exp2((m - mn) * sl2) : 1.f;
+      l *= alpha;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) o16[b] *= alpha;
+      m = mn;
+    }
+    const float mu2 = (m == kNegInf) ? 0.f : m * sl2;
+    V8 pb;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float e = fast_exp2(fmaf(s[b][j], sl2, -mu2));
+        l += e;
+        pb[4 * b + j] = (T)e;
+      }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      u32x2 part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const LDS_AS char* pp = (const LDS_AS char*)vlane + 16 * h * kVRowBytes + db * 32;
+        part[h] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)pp));
+      }
+      const u32x4 w = {part[0][0], part[0][1], part[1][0], part[1][1]};
+      o16[db] = Dt<T>::mfma16(__builtin_bit_cast(V8, w), pb, o16[db]);
+    }
+  };
   auto compute = [&](int kb) __attribute__((always_inline)) {
+    if constexpr (kCols == 16) {
+      compute16(kb);
+      return;
+    }
     f32x16 s[1];
     s[0] = f32x16{};
 #pragma unroll
@@ -1112,7 +1210,12 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
       }
     }
   }
-  l = xhalf_sum(l);
+  if constexpr (kCols == 32) {
+    l = xhalf_sum(l);
+  } else {
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+  }
 
   // ---- merge the wave states in LDS
   __syncthreads();
@@ -1122,28 +1225,41 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
   int* sm_flag = reinterpret_cast<int*>(accs + 4 * kHeadDim * 32);
   // wave maxima in scaled (base-2) units
   const float m2 = (m == kNegInf) ? kNegInf : m * sl2;
-  if (hi == 0) sm_m[wave * 32 + r32] = m2;
+  // one lane per row writes the row statistics: lane half 0 (32 columns) or
+  // lane group 0 (16 columns)
+  const bool stat_lane = kCols == 32 ? hi == 0 : q16 == 0;
+  if (stat_lane) sm_m[wave * 32 + col] = m2;
   __syncthreads();
   float M = kNegInf;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 32 + r32]);
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w * 32 + col]);
   const float sc = (M == kNegInf) ? 0.f : fast_exp2(m2 - M);
-  if (hi == 0) sm_l[wave * 32 + r32] = l * sc;
-  // waves w and w + 4 sum into partial sum w % 4
+  if (stat_lane) sm_l[wave * 32 + col] = l * sc;
+  // waves w and w + 4 sum into partial sum w % 4 ([d][32 rows]; 16 columns
+  // fill rows 0-15)
   float* acc = accs + (wave & 3) * kHeadDim * 32;
-  if (wave < 4) {
+  auto put = [&](bool add) __attribute__((always_inline)) {
+    if constexpr (kCols == 32) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[(db * 32 + acc_d(j, hi)) * 32 + r32] = o[db][j] * sc;
-  }
+        for (int j = 0; j < 16; ++j) {
+          float& a = acc[(db * 32 + acc_d(j, hi)) * 32 + r32];
+          a = add ? a + o[db][j] * sc : o[db][j] * sc;
+        }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float& a = acc[(16 * db + 4 * q16 + j) * 32 + col];
+          a = add ? a + o16[db][j] * sc : o16[db][j] * sc;
+        }
+    }
+  };
+  if (wave < 4) put(false);
   __syncthreads();
-  if (wave >= 4) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[(db * 32 + acc_d(j, hi)) * 32 + r32] += o[db][j] * sc;
-  }
+  if (wave >= 4) put(true);
   __syncthreads();
 
   // final stage on the first 256 threads: row threadIdx / 8, 16 dims each
@@ -1302,10 +1418,16 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
     const RoleView r = pick_role(p, flags & kFlagRole, kvh);
     CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
     const RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
-    if ((flags & kFlagRole) && p.role[1].kv_fp8)
-      chunk_item<T, true>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
+    const bool fp8 = (flags & kFlagRole) && p.role[1].kv_fp8;
+    const bool narrow = rg.qo_len * p.group_size <= 16;   // 16x16x32 MFMAs
+    if (fp8 && narrow)
+      chunk_item<T, true, 16>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
+    else if (fp8)
+      chunk_item<T, true, 32>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
+    else if (narrow)
+      chunk_item<T, false, 16>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
     else
-      chunk_item<T, false>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
+      chunk_item<T, false, 32>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
   };
   auto run_chunks = [&]() {
     for (int j = 0; j < n_chunks; ++j) {
