@@ -284,6 +284,25 @@ __device__ __forceinline__ uint64_t row_off(const RoleView& r, PArg p, uint32_t 
   return (uint64_t)page * r.kv_sp_b + (uint32_t)slot * r.kv_st_b;
 }
 
+// Where one wave's key rows of a key chunk come from: pool bases of the item's
+// kv head, page table and strides, the wave's first key, the chunk's last key.
+struct KeySrc {
+  const char* k;
+  const char* v;
+  const int32_t* indices;
+  uint32_t sp_b, st_b;
+  int page_start, first, last;
+};
+
+// The loads a 16-bit key chunk keeps in flight at the top of its step loop:
+// the rows of the current step and the page ids of the one after. A chunk
+// issues them for the next chunk of the workgroup's list while it merges its
+// waves and stores its output, so the load stream does not stop there.
+struct ChunkCarry {
+  uint32_t pidx[8];
+  u32x4 kst[8], vst[8];
+};
+
 // Q^T operand of one row: lane half hi holds d = hi*64 + c*8 + [0,8) for MFMA c.
 template <typename T>
 __device__ __forceinline__ void load_q(typename Dt<T>::v8 (&qreg)[8], const RoleView& r,
@@ -953,9 +972,14 @@ __device__ __forceinline__ void fp8x16_widen(const u32x4 w, u32x4& c0, u32x4& c1
 // its P^T operand (slot 8(lane/16) + e), so the V^T operand reads keys 4(lane/16)
 // + [0,4) and 16 + 4(lane/16) + [0,4); head dims go to lane group q = lane/16 as
 // d = 32q + 8c + [0,8) in the c-th score MFMA.
+// cc / carried: the loads of this chunk's first step when the previous chunk
+// issued them (carried), and on return those of item next_idx (>= 0: the next
+// item of the list, of the same kind) when the rows are 16-bit and the chunk
+// has at most 16 query rows (the wider form has no registers to spare).
 template <typename T, bool kFp8, int kCols>
 __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowGeom& rg, int kvh,
-                           int kv_begin, int kv_end, int split, int grp, char* lds, int wave_s) {
+                           int kv_begin, int kv_end, int split, int grp, char* lds, int wave_s,
+                           ChunkCarry& cc, bool& carried, int next_idx) {
   using V8 = typename Dt<T>::v8;
   // the thread index, rebuilt from the wave (scalar) and the lane count, so the
   // hardware's thread-id register need not live through the whole launch; and
@@ -1020,7 +1044,8 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
     vlane = Vw + (4 * q16 + ((lane & 15) >> 2)) * kVRowBytes + 8 * (lane & 3);
   }
 
-  const int first = kv_begin + kStepKeys * wave;
+  // the wave's first key and step count from the scalar wave index (uniform)
+  const int first = kv_begin + kStepKeys * wave_s;
   const int n_steps = first < kv_end ? (kv_end - first + kWaves * kStepKeys - 1) / (kWaves * kStepKeys) : 0;
   // one step's scores, softmax and P.V from the wave's LDS blocks (keys kb..)
   auto compute16 = [&](int kb) __attribute__((always_inline)) {
@@ -1106,28 +1131,48 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
   if constexpr (!kFp8) {
     // loads: instruction c moves row 4c + (lane >> 4) of the step, slot lane & 15
     const int ld_row = lane >> 4, ld_slot = lane & 15;
-    uint32_t pidx[8];
-    u32x4 kst[8], vst[8];
-    auto load_pages = [&](int i) {
-      const int kb = step_kb(i);
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-        pidx[c] = page_of(r, p, rg.page_start, min(kb + 4 * c + ld_row, kv_end - 1));
-    };
-    // rows past kv_end repeat row kv_end - 1 (masked to zero weight)
-    auto load_rows = [&](int i) {
-      const int kb = step_kb(i);
+    uint32_t (&pidx)[8] = cc.pidx;
+    u32x4 (&kst)[8] = cc.kst;
+    u32x4 (&vst)[8] = cc.vst;
+    const KeySrc cur{r.k, r.v, r.indices, r.kv_sp_b, r.kv_st_b, rg.page_start, first, kv_end - 1};
+    // the next item, when its rows load the same way and this wave has keys in it
+    KeySrc nxt = cur;
+    bool has_next = false;
+    if (kCols == 16 && next_idx >= 0) {
+      CI32* it = plan_words(image_region(p, kHdrItems)) + next_idx * kItemWords;
+      const int nfirst = it[5] + kStepKeys * wave_s;
+      if (nfirst < it[6]) {
+        const RoleView r2 = pick_role(p, it[0] & kFlagRole, it[2]);
+        CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
+        nxt = KeySrc{r2.k, r2.v, r2.indices, r2.kv_sp_b, r2.kv_st_b, rq[3], nfirst, it[6] - 1};
+        has_next = true;
+      }
+    }
+    // rows past the chunk's end repeat its last row (masked to zero weight)
+    auto pages_of = [&](const KeySrc& s, int i) __attribute__((always_inline)) {
+      const int kb = s.first + kWaves * kStepKeys * i;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const uint64_t off = row_off(r, p, pidx[c], min(kb + 4 * c + ld_row, kv_end - 1));
-        kst[c] = ld16(r.k + off + ((ld_slot ^ swz(4 * c + ld_row)) << 4));
-        vst[c] = ld16(r.v + off + (ld_slot << 4));
+        const int key = min(kb + 4 * c + ld_row, s.last);
+        const int pg = p.page_shift >= 0 ? (key >> p.page_shift) : key / p.page_size;
+        pidx[c] = s.indices ? (uint32_t)s.indices[s.page_start + pg] : (uint32_t)(s.page_start + pg);
       }
     };
-    if (n_steps > 0) {
-      load_pages(0);
-      load_rows(0);
-      if (n_steps > 1) load_pages(1);
+    auto rows_of = [&](const KeySrc& s, int i) __attribute__((always_inline)) {
+      const int kb = s.first + kWaves * kStepKeys * i;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int key = min(kb + 4 * c + ld_row, s.last);
+        const int slot = p.page_shift >= 0 ? (key & (p.page_size - 1)) : key % p.page_size;
+        const uint64_t off = (uint64_t)pidx[c] * s.sp_b + (uint32_t)slot * s.st_b;
+        kst[c] = ld16(s.k + off + ((ld_slot ^ swz(4 * c + ld_row)) << 4));
+        vst[c] = ld16(s.v + off + (ld_slot << 4));
+      }
+    };
+    if (!carried && n_steps > 0) {
+      pages_of(cur, 0);
+      rows_of(cur, 0);
+      if (n_steps > 1) pages_of(cur, 1);
     }
     for (int i = 0; i < n_steps; ++i) {
       // this step's rows to the wave's blocks; the previous step's reads of them
@@ -1138,10 +1183,19 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
         lds_st16(Vw, (4 * c + ld_row) * kVRowBytes + (ld_slot << 4), vst[c]);
       }
       if (i + 1 < n_steps) {
-        load_rows(i + 1);
-        if (i + 2 < n_steps) load_pages(i + 2);
+        rows_of(cur, i + 1);
+        if (i + 2 < n_steps)
+          pages_of(cur, i + 2);
+        else if (has_next)
+          pages_of(nxt, 0);   // a step ahead, as within the chunk
       }
       compute(step_kb(i));
+    }
+    carried = has_next;
+    if (has_next) {
+      if (n_steps < 2) pages_of(nxt, 0);
+      rows_of(nxt, 0);
+      pages_of(nxt, 1);
     }
   } else {
     // FP8 rows are 128 bytes: instruction c moves row 8c + (lane >> 3) of the
@@ -1209,6 +1263,7 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
         if (i + 1 < n_steps) compute(step_kb(i + 1));
       }
     }
+    carried = false;
   }
   if constexpr (kCols == 32) {
     l = xhalf_sum(l);
@@ -1388,6 +1443,42 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
   if (tid == 0) atomicExch(image_region(p, kHdrCounters) + grp, 0);
 }
 
+// Kind of a key-chunk item: bit 1 FP8 rows, bit 0 at most 16 rows (16x16x32
+// MFMAs).
+__device__ __forceinline__ int chunk_kind(PArg p, int idx) {
+  CI32* it = plan_words(image_region(p, kHdrItems)) + idx * kItemWords;
+  CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
+  const bool fp8 = (it[0] & kFlagRole) && p.role[1].kv_fp8;
+  const bool narrow = rq[1] * p.group_size <= 16;
+  return 2 * fp8 + narrow;
+}
+
+// Key-chunk items idx0, idx0 + 1, ... (below end) while they are of this kind,
+// the first step's loads of each issued in the previous one's tail. Returns
+// how many ran (at least one).
+template <typename T, bool kFp8, int kCols>
+__device__ __forceinline__ int chunk_items(PArg p, int idx0, int end, char* lds, int wave_s) {
+  constexpr int kKind = 2 * kFp8 + (kCols == 16);
+  ChunkCarry cc;
+  bool carried = false;
+  int idx = idx0;
+  for (;;) {
+    const int next = idx + 1 < end && chunk_kind(p, idx + 1) == kKind ? idx + 1 : -1;
+    CI32* it = plan_words(image_region(p, kHdrItems)) + idx * kItemWords;
+    const int flags = it[0];
+    const int kvh = it[2], kv_begin = it[5], kv_end = it[6], grp = it[7];
+    const RoleView r = pick_role(p, flags & kFlagRole, kvh);
+    CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
+    const RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
+    chunk_item<T, kFp8, kCols>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s,
+                               cc, carried, next);
+    if (next < 0) break;
+    __syncthreads();   // the item is done with the LDS
+    idx = next;
+  }
+  return idx + 1 - idx0;
+}
+
 // One persistent workgroup per CU runs its static list from the plan: its key
 // chunks one after another, and its query tiles as one block stream (chunks
 // first or last, as the plan says). Then it takes key chunks from the shared
@@ -1411,28 +1502,21 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
   const int first_item = wg[0], n_tiles = wg[1], n_chunks = wg[2];
   const int first_blk = wg[3], n_blk = wg[4];
   const bool chunks_first = wg[5] != 0;
-  auto run_chunk = [&](int idx) __attribute__((always_inline)) {
-    CI32* it = plan_words(image_region(p, kHdrItems)) + idx * kItemWords;
-    const int flags = it[0];
-    const int kvh = it[2], kv_begin = it[5], kv_end = it[6], grp = it[7];
-    const RoleView r = pick_role(p, flags & kFlagRole, kvh);
-    CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
-    const RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
-    const bool fp8 = (flags & kFlagRole) && p.role[1].kv_fp8;
-    const bool narrow = rg.qo_len * p.group_size <= 16;   // 16x16x32 MFMAs
-    if (fp8 && narrow)
-      chunk_item<T, true, 16>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
-    else if (fp8)
-      chunk_item<T, true, 32>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
-    else if (narrow)
-      chunk_item<T, false, 16>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
-    else
-      chunk_item<T, false, 32>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s);
+  // the items idx .. end - 1 of the list while they are of one kind; returns
+  // how many ran
+  auto run_chunk_items = [&](int idx, int end) __attribute__((always_inline)) {
+    switch (chunk_kind(p, idx)) {
+      case 3: return chunk_items<T, true, 16>(p, idx, end, lds, wave_s);
+      case 2: return chunk_items<T, true, 32>(p, idx, end, lds, wave_s);
+      case 1: return chunk_items<T, false, 16>(p, idx, end, lds, wave_s);
+      default: return chunk_items<T, false, 32>(p, idx, end, lds, wave_s);
+    }
   };
-  auto run_chunks = [&]() {
-    for (int j = 0; j < n_chunks; ++j) {
+  auto run_chunks = [&]() __attribute__((always_inline)) {
+    const int c0 = first_item + n_tiles;
+    for (int j = 0; j < n_chunks;) {
       __syncthreads();   // the previous item is done with the LDS
-      run_chunk(first_item + n_tiles + j);
+      j += run_chunk_items(c0 + j, c0 + n_chunks);
     }
   };
   if (chunks_first) run_chunks();
@@ -1464,7 +1548,8 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
       __syncthreads();
       const int j = __builtin_amdgcn_readfirstlane(pool_slot);
       if (j >= pool_count) break;
-      run_chunk(hdr_word(p, kHdrPoolFirst) + j);
+      const int idx = hdr_word(p, kHdrPoolFirst) + j;
+      run_chunk_items(idx, idx + 1);
     }
     // every workgroup has taken its last (empty) turn before it counts itself
     // done, so the last one can clear both counters

@@ -20,7 +20,7 @@ def log(msg):
 
 
 def plan_and_run(w, roles=("prefill", "decode"), decode_chunk=0, order=0, ws_mb=256,
-                 return_lse=True, pod=None, poison_out=False):
+                 return_lse=True, pod=None, poison_out=False, identity_pages_d=False):
     spec = w.spec
     p = w.prefill if "prefill" in roles else None
     d = w.decode if "decode" in roles else None
@@ -49,7 +49,8 @@ def plan_and_run(w, roles=("prefill", "decode"), decode_chunk=0, order=0, ws_mb=
             l.fill_(float("nan"))
         outs[name] = (o, l)
     res = pod.run(p.q if p else None, p.kv_cache if p else None, p.kv_indices_dev if p else None,
-                  d.q if d else None, d.kv_cache if d else None, d.kv_indices_dev if d else None,
+                  d.q if d else None, d.kv_cache if d else None,
+                  d.kv_indices_dev if d is not None and not identity_pages_d else None,
                   sinks=w.sinks if spec.sinks else None, return_lse=return_lse,
                   out_p=outs["p"][0], out_d=outs["d"][0],
                   lse_p=outs["p"][1] if return_lse else None, lse_d=outs["d"][1] if return_lse else None,

@@ -91,6 +91,46 @@ def test_split_kv_merge(chunk):
     check_all(w, res, f"split{chunk}")
 
 
+MANY = [
+    dict(dtype="bf16", ps=16, w=-1, sinks=False, chunk=0, identity=False),
+    dict(dtype="f16", ps=5, w=90, sinks=True, chunk=0, identity=True),
+    dict(dtype="bf16", ps=16, w=-1, sinks=True, chunk=128, identity=False),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(MANY)), ids=[str(i) for i in range(len(MANY))])
+def test_many_chunks_per_workgroup(idx):
+    """More key-chunk items than workgroups, so each workgroup runs a list of
+    them back to back and issues a chunk's first loads in the previous one's
+    tail. Ragged lengths leave waves without keys in some chunks; requests of
+    one and of three rows (group 8: 8 and 24 rows) put chunks of both widths
+    in one list; split groups and an identity page table (no kv_indices) are
+    covered too."""
+    cfg = MANY[idx]
+    rng = np.random.default_rng(40 + idx)
+    n = 640
+    q_lens = rng.choice([1, 1, 1, 3], n).tolist()
+    kv_lens = [int(max(k, q)) for k, q in zip(rng.integers(1, 700, n), q_lens)]
+    spec = WorkloadSpec(
+        name="many_chunks", prefill=None,
+        decode=RoleSpec(q_lens, kv_lens, causal=True, window_left=cfg["w"]),
+        num_qo_heads=16, num_kv_heads=2, page_size=cfg["ps"], dtype=cfg["dtype"], sinks=cfg["sinks"],
+        pool="separate", shuffle_pages=not cfg["identity"], spare_pages=0, meta_seed=300 + idx,
+        value_seed=400 + idx)
+    log(f"case: many chunks per workgroup {idx} {cfg}")
+    w = build(spec, device="cuda")
+    if cfg["identity"]:
+        assert np.array_equal(w.decode.kv_indices, np.arange(len(w.decode.kv_indices)))
+    res, pod = plan_and_run(w, roles=("decode",), decode_chunk=cfg["chunk"],
+                            identity_pages_d=cfg["identity"])
+    info = pod.plan_info()
+    log(f"plan: {info}")
+    assert info["n_items"] > 2 * info["grid"]
+    if cfg["chunk"]:
+        assert info["n_groups"] > 0
+    check_all(w, res, f"many{idx}")
+
+
 def test_repeat_runs_are_bitwise_stable_and_counters_reset():
     log("case: repeated runs with split-KV")
     w = build(small_spec(dq=2, sinks=True), device="cuda")
