@@ -236,8 +236,9 @@ int pod_destroy(pod_ctx_t ctx);
  * device. Plans alternate between the two halves of the int workspace; the copy
  * runs on a stream the context owns, once the launches of the plan before last
  * (which read the same half) have finished (the host waits for that if needed),
- * so it overlaps the previous plan's launches. The next pod_run() waits for the copy (on its own stream), so no
- * further ordering is needed. `stream` is unused (kept for symmetry with
+ * so it overlaps the previous plan's launches. pod_plan returns once that copy
+ * has completed (a host wait on the context's own copy stream, not on any
+ * launch), so pod_run() needs no further ordering. `stream` is unused (kept for symmetry with
  * pod_run). Not to be called during stream capture. Replaces any previous plan
  * of this context.
  */
@@ -247,9 +248,9 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream);
 int pod_plan_stats(pod_ctx_t ctx, pod_plan_info* info);
 
 /*
- * Enqueue the fused attention launch on `stream`: a wait for the current plan's
- * work-list copy, then exactly one kernel launch (none if the plan holds no
- * work). Buffers must match the plan's shapes and dtype. Asynchronous;
+ * Enqueue the fused attention launch on `stream`: exactly one kernel launch
+ * (none if the plan holds no work; the plan's work list is already on the
+ * device). Buffers must match the plan's shapes and dtype. Asynchronous;
  * allocates nothing; leaves the workspace counters at zero when the launch
  * completes, so runs can be repeated without a re-plan.
  */

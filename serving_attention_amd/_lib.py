@@ -42,9 +42,10 @@ _i32p = ctypes.POINTER(ctypes.c_int32)
 class PodRoleDesc(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32),
-        ("qo_indptr", _i32p),
-        ("kv_indptr", _i32p),
-        ("last_page_len", _i32p),
+        # host int32 arrays, as addresses (a plain integer or None)
+        ("qo_indptr", ctypes.c_void_p),
+        ("kv_indptr", ctypes.c_void_p),
+        ("last_page_len", ctypes.c_void_p),
         ("causal", ctypes.c_int32),
         ("window_left", ctypes.c_int32),
         ("sm_scale", ctypes.c_float),

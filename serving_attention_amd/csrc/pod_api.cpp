@@ -293,7 +293,13 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (work list)");
   e = hipEventRecord(ctx->staged[k], ctx->copy_stream);
   if (e != hipSuccess) return hip_err(e, "hipEventRecord");
-  ctx->staged_pending[k] = true;
+  // The host waits for this copy (a few microseconds on the library's own
+  // stream; launches already queued keep running), so pod_run enqueues the
+  // launch alone: a cross-stream wait ahead of each launch measured 2-5 us
+  // slower per step.
+  e = hipEventSynchronize(ctx->staged[k]);
+  if (e != hipSuccess) return hip_err(e, "hipEventSynchronize");
+  ctx->staged_pending[k] = false;
   ctx->cur = k;
   ctx->next_staging = 1 - k;
   }
@@ -413,7 +419,8 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     g_err.clear();
     return POD_OK;
   }
-  // this plan's work list must be up; a stream wait only while its copy runs
+  // this plan's work list must be up (pod_plan waited for its copy; the
+  // stream wait stays for safety and is not taken)
   hipError_t he = hipSuccess;
   if (ctx->staged_pending[ctx->cur]) {
     he = hipEventQuery(ctx->staged[ctx->cur]);

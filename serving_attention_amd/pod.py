@@ -22,6 +22,8 @@ KVCache = Union[torch.Tensor, Tuple[torch.Tensor, torch.Tensor]]
 
 
 def _host_i32(x) -> np.ndarray:
+    if type(x) is np.ndarray and x.dtype == np.int32 and x.flags.c_contiguous:
+        return x
     if isinstance(x, torch.Tensor):
         x = x.detach().to("cpu")
         x = x.numpy()
@@ -29,9 +31,10 @@ def _host_i32(x) -> np.ndarray:
 
 
 def _ptr(a: Optional[np.ndarray]):
+    """Address of a host array's data (the plan descriptor's pointer fields)."""
     if a is None:
         return None
-    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    return a.__array_interface__["data"][0]
 
 
 def _dtype_code(dtype) -> int:
@@ -152,11 +155,18 @@ class BatchPOD:
             raise NotImplementedError(f"decode K/V dtype {kv_dtype_d} is not supported")
         s = _stream_handle(self.device) if stream is None else ctypes.c_void_p(stream)
         _lib.check(self._lib.pod_plan(self._ctx, ctypes.byref(desc), s))
+        # keep holds (qo, kv, lpl) of each role that is present, prefill first
         nnz = []
         rows = []
-        for qo, kv in ((qo_indptr_p, kv_indptr_p), (qo_indptr_d, kv_indptr_d)):
-            rows.append(int(_host_i32(qo)[-1]) if qo is not None else 0)
-            nnz.append(int(_host_i32(kv)[-1]) if kv is not None else 0)
+        k = 0
+        for qo in (qo_indptr_p, qo_indptr_d):
+            if qo is None:
+                rows.append(0)
+                nnz.append(0)
+            else:
+                rows.append(int(keep[k][-1]))
+                nnz.append(int(keep[k + 1][-1]))
+                k += 3
         self._planned = dict(
             rows=tuple(rows), nnz=tuple(nnz),
             num_qo_heads=int(num_qo_heads), num_kv_heads=int(num_kv_heads),

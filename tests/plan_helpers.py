@@ -17,7 +17,7 @@ def role_desc(qo_lens, kv_lens, page_size, causal=True, window_left=-1, keep=Non
     kv = np.asarray(kv_indptr, np.int32)
     lpl = np.asarray(last_page_len if last_page_len is not None else [(k - 1) % page_size + 1 for k in kv_lens], np.int32)
     keep.extend([qo, kv, lpl])
-    p = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    p = lambda a: a.ctypes.data
     return _lib.PodRoleDesc(len(qo) - 1, p(qo), p(kv), p(lpl), int(causal), window_left, float(sm_scale))
 
 
