@@ -218,14 +218,14 @@ def test_workgroup_lists(wl, order):
         else:
             assert chunks_first == 0
     assert nxt == pf
-    # the shared pool: key chunks only, heaviest first, at most a quarter of
+    # the shared pool: key chunks only, heaviest first, at most a tenth of
     # the chunks' estimated cost, and none heavier than a chunk left in a list
     pool = items[pf:]
     assert all(int(c[0]) & FLAG_CHUNK for c in pool)
     pc_cost = [item_cost(c) for c in pool]
     assert pc_cost == sorted(pc_cost, reverse=True)
     chunk_costs = [item_cost(c) for c in items if int(c[0]) & FLAG_CHUNK]
-    assert sum(pc_cost) <= 0.25 * sum(chunk_costs) + 1
+    assert sum(pc_cost) <= 0.10 * sum(chunk_costs) + 1
     listed = [item_cost(c) for c in items[:pf] if int(c[0]) & FLAG_CHUNK]
     if pool.size and listed:
         assert max(pc_cost) <= min(listed)
