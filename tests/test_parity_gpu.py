@@ -272,3 +272,23 @@ def test_named_pod_chunked():
     assert_close(w, errs, "pod_chunked/decode")
     del w
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w,dq,hqo", [(-1, 1, 16), (50, 3, 16), (0, 2, 16), (200, 5, 64)])
+def test_non_causal_roles(w, dq, hqo):
+    """Both roles without the causal mask: every row sees keys up to kv_len - 1,
+    and a window bounds them on the left at (diagonal - window_left), the
+    reading taken where the pages give the window only for causal rows. Prefill
+    chunks sit on prefixes (qo_len < kv_len); with hqo 64 / 4 kv heads the
+    multi-token decode rows (group 16 x q_len 5 > 32) run as query tiles."""
+    log(f"case: non-causal roles (window_left={w}, q_len_d={dq}, hqo={hqo})")
+    d_kv = (5, 40, 300, 1000)
+    spec = WorkloadSpec(
+        name="noncausal",
+        prefill=RoleSpec([60, 130, 1], [60, 400, 90], causal=False, window_left=w),
+        decode=RoleSpec([dq] * len(d_kv), [max(k, dq) for k in d_kv], causal=False, window_left=w),
+        num_qo_heads=hqo, num_kv_heads=4, page_size=16, dtype="bf16", sinks=False, pool="shared",
+        shuffle_pages=True, spare_pages=3, meta_seed=311, value_seed=411)
+    wl = build(spec, device="cuda")
+    res, _ = plan_and_run(wl)
+    check_all(wl, res, f"noncausal-w{w}-q{dq}")
