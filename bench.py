@@ -6,7 +6,10 @@ and resident in HBM before the timed region. Per layer the KV cache and the
 queries differ, as in the per-layer loop of the POD article's examples, so a
 step does not find the previous step's KV in the caches.
 
-Prints one JSON line. `value` is the mean step latency in microseconds.
+Prints one JSON line. `value` is the mean step latency in microseconds. The
+default workload is the chunked-prefill POD step at serving scale (a 4096-token
+chunk on a 16384-token prefix plus 256 four-token decodes, window 4096, sinks);
+the other named workloads run with --workload.
 """
 from __future__ import annotations
 
@@ -209,11 +212,23 @@ def cpu_baseline(w, budget_s):
 
     import oracle
 
-    threads = None
+    threads, blas = None, None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=None)
+        pools = threadpool_info()
+        threads = max((i.get("num_threads", 0) for i in pools), default=None)
+        blas = "; ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer')}, "
+                         f"{i.get('num_threads')} threads)" for i in pools if i.get("user_api") == "blas")
     except Exception:
+        pass
+    cpu_model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
         pass
     spec = w.spec
     sinks = w.sinks.cpu().numpy() if spec.sinks else None
@@ -253,7 +268,7 @@ def cpu_baseline(w, budget_s):
             "kind": "oracle",
             "sample": "fp64 numpy oracle timed on " + "; ".join(parts) +
                       " (last rows of randomly chosen requests), scaled by rows to one step",
-            "host_cpus": os.cpu_count(), "host": platform.processor() or platform.machine()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model, "blas": blas or "unknown"}
 
 
 CASCADE = dict(prefix=1536, suffix=512, requests=128, num_qo_heads=64, num_kv_heads=8, page_size=16)
@@ -423,7 +438,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="pod", choices=sorted(DESCR))
+    ap.add_argument("--workload", default="pod_chunked", choices=sorted(DESCR))
     ap.add_argument("--layers", type=int, default=None,
                     help="distinct KV caches / queries cycled per step (default: 4, 1 for pod_chunked)")
     ap.add_argument("--decode-chunk", type=int, default=0)

@@ -101,15 +101,22 @@ typedef struct pod_role_desc {
  *                 (pod_plan_compute / pod_workspace_bytes).
  *   decode_chunk  keys per split of a decode request: 0 = planner's choice,
  *                 -1 = never split, else rounded up to a multiple of 64.
- *   order         POD_ORDER_* policy for how prefill and decode items share the grid:
- *                 INTERLEAVE (default) mixes them in proportion to their estimated
- *                 cost, decode slightly ahead; PREFILL_FIRST / DECODE_FIRST run one
- *                 role's items before the other's; LONGEST_FIRST takes the items of
- *                 both roles heaviest first. Any other value is POD_ERR_INVALID.
+ *   order         POD_ORDER_* policy for when a persistent workgroup runs its key
+ *                 chunks (decode-style items) relative to its query tiles
+ *                 (prefill-style items); every workgroup's list holds both kinds in
+ *                 proportion to their estimated cost, placed by die:
+ *                 INTERLEAVE (default): workgroups w with (w / 8) odd run their key
+ *                 chunks first, the others their query tiles first, so half of each
+ *                 die's workgroups start on each kind and both kinds run at once;
+ *                 PREFILL_FIRST / DECODE_FIRST: every workgroup runs its query tiles
+ *                 / its key chunks first; LONGEST_FIRST: a workgroup runs its key
+ *                 chunks first when its heaviest key chunk costs more than its
+ *                 heaviest query tile of either role. Results do not depend on the
+ *                 order. Any other value is POD_ERR_INVALID.
  *   decode_kv_dtype  element type of the decode role's K/V pools: 0 = `dtype`, or
  *                 POD_DTYPE_FP8_E4M3 (OCP E4M3, 1 byte, strides still in elements):
  *                 the FP8 KV cache whose calibration scales the POD article lists
- *                 with the decode run parameters ([POD] "Prefill 侧参数"). q and O stay
+ *                 with the decode run parameters ([POD] "Decode 侧参数与'plan 覆盖'行为"). q and O stay
  *                 `dtype`; values are widened exactly to `dtype` inside the launch.
  *                 Supported only where every decode (request, kv head) runs as one
  *                 key-chunk item, i.e. q_len * group <= 32 rows (POD_ERR_UNSUPPORTED
@@ -167,10 +174,14 @@ typedef struct pod_role_args {
 /*
  * sinks: device fp32 [num_qo_heads]; required iff the plan had has_sinks.
  * q_scale_d, k_scale_d, v_scale_d: the decode role's calibration scales for an
- * FP8 KV cache ([POD] "Prefill 侧参数"): q_scale_d * k_scale_d multiply the
+ * FP8 KV cache ([POD] "Decode 侧参数与'plan 覆盖'行为": the only decode
+ * parameters that take effect at run time): q_scale_d * k_scale_d multiply the
  * decode sm_scale, v_scale_d multiplies the decode output (folded into the
  * launch's final normalisation, before the cast to `dtype`; the LSE does not
- * see it). 0 means 1.0; any value is accepted for any decode_kv_dtype.
+ * see it). 0 means 1.0; they apply to any decode_kv_dtype. Each must be finite,
+ * q_scale_d * k_scale_d must be > 0 and sm_scale_d * q_scale_d * k_scale_d must
+ * stay <= 1e6 (the bound plan puts on sm_scale); otherwise pod_run returns
+ * POD_ERR_INVALID and enqueues nothing.
  */
 typedef struct pod_run_args {
   pod_role_args prefill;
@@ -228,31 +239,60 @@ int pod_create_graph(pod_ctx_t* out, int device, void* float_ws, size_t float_ws
                      void* int_ws, size_t int_ws_bytes, int32_t prefill_batch,
                      int32_t decode_batch);
 
-/* Release the context's host state and staging buffers. NULL is accepted. */
+/*
+ * Release the context's host state, staging buffers, events and copy stream
+ * after the launches and copies it issued have completed ([POD] "使用建议与已知
+ * 限制": the workspaces stay the caller's, on the caller's device). The caller's
+ * workspaces are not freed. NULL is accepted; returns POD_OK.
+ */
 int pod_destroy(pod_ctx_t ctx);
 
 /*
- * Validate `desc`, build the work list on the host and start its copy to the
- * device. Plans alternate between the two halves of the int workspace; the copy
- * runs on a stream the context owns, once the launches of the plan before last
- * (which read the same half) have finished (the host waits for that if needed),
- * so it overlaps the previous plan's launches. pod_plan returns once that copy
- * has completed (a host wait on the context's own copy stream, not on any
- * launch), so pod_run() needs no further ordering. `stream` is unused (kept for symmetry with
- * pod_run). Not to be called during stream capture. Replaces any previous plan
- * of this context.
+ * Build the work list from host length arrays and put it on the device: what
+ * the pages' plan() does ([POD] "plan 内部做了什么": per-request KV lengths from
+ * the page counts and last_page_len, split-KV decisions, the auxiliary data that
+ * later runs reuse; "plan/run 生命周期": plan before any run, cached for many
+ * runs; "Batch 版本 plan 的 colocated-CTA 调度细节": how the two roles share the
+ * device). Unlike the pages' plan it takes no page indices: the work list
+ * depends on lengths only, and kv_indices are pod_run arguments.
+ *   Default context: plans alternate between the two halves of the int
+ *   workspace. The copy runs on a stream the context owns, once the launches of
+ *   the plan before last (which read the same half) have finished (the host
+ *   waits for them only if they are still running), so it overlaps the
+ *   previous plan's launches; pod_plan then waits on the host for that copy
+ *   alone (a few microseconds), so pod_run needs no stream-ordering of its own.
+ *   `stream` is not used in this mode.
+ *   Graph context (pod_create_graph): the copy is enqueued on `stream`, ahead of
+ *   the launches that follow there; pod_plan does not wait for it.
+ * Errors: POD_ERR_INVALID / POD_ERR_UNSUPPORTED for descriptors the planner
+ * rejects (the pages' ValueError / NotImplementedError cases),
+ * POD_ERR_WORKSPACE if either workspace is too small for this plan, POD_ERR_HIP
+ * for a failed copy; on any error the previous plan stays in force. Not to be
+ * called during stream capture ([POD] "plan/run 生命周期"). Replaces any
+ * previous plan of this context.
  */
 int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream);
 
-/* Info about the context's current plan. */
+/*
+ * Counts of the context's current plan (the auxiliary data the pages' plan
+ * caches for run, [POD] "plan/run 生命周期"). POD_ERR_NOT_PLANNED before the
+ * first successful pod_plan.
+ */
 int pod_plan_stats(pod_ctx_t ctx, pod_plan_info* info);
 
 /*
- * Enqueue the fused attention launch on `stream`: exactly one kernel launch
- * (none if the plan holds no work; the plan's work list is already on the
- * device). Buffers must match the plan's shapes and dtype. Asynchronous;
+ * The pages' run() ([POD] "run 参数详解": one call produces both roles'
+ * outputs; "BatchPOD 的 run 差异": every policy parameter comes from the plan,
+ * and the batch wrapper returns both LSEs). Enqueues the fused attention
+ * launch on `stream`: exactly one kernel launch (none if the plan holds no
+ * work; the plan's work list is already on the device). Buffers must match the
+ * plan's shapes and dtype; they are not read on the host. Asynchronous;
  * allocates nothing; leaves the workspace counters at zero when the launch
- * completes, so runs can be repeated without a re-plan.
+ * completes, so runs can be repeated without a re-plan. Errors (nothing is
+ * enqueued): POD_ERR_NOT_PLANNED before a plan or for sinks that contradict it,
+ * POD_ERR_INVALID for NULL required buffers, non-positive or misaligned
+ * strides and bad scales (see pod_run_args), POD_ERR_UNSUPPORTED for pool
+ * strides of 2^30 elements or more, POD_ERR_HIP if the launch fails.
  */
 int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream);
 
@@ -279,15 +319,30 @@ int pod_merge_states(const void* o_a, const float* lse_a, const void* o_b, const
                      void* o_out, float* lse_out, int64_t rows, int num_heads, int head_dim,
                      int dtype, const float* sinks, int device, void* stream);
 
-/* Message for the calling thread's last failed call ("" if none). */
+/*
+ * Message for the calling thread's last failed call ("" after a success). The
+ * codes map to the pages' Python conventions: POD_ERR_INVALID is the
+ * ValueError the wrappers raise for inputs that break their constraints
+ * ([POD] "CUDAGraph 模式的运行时约束": mismatched batch sizes and buffers),
+ * POD_ERR_UNSUPPORTED their NotImplementedError. The string stays valid until
+ * the thread's next call into the library.
+ */
 const char* pod_last_error(void);
 
-/* Workspace sizes `desc` needs (host only; no device access). */
+/*
+ * Workspace sizes the plan of `desc` needs (host only; no device access):
+ * float_ws_bytes for split-KV partial states, int_ws_bytes for the work list
+ * (two alternating images). The pages recommend a 128 MB float workspace
+ * ([POD] "使用建议与已知限制"); this query gives the exact need, which grows with
+ * the number of split decode chunks. Either output pointer may be NULL.
+ * Errors as pod_plan's validation (POD_ERR_INVALID / POD_ERR_UNSUPPORTED).
+ */
 int pod_workspace_bytes(const pod_plan_desc* desc, size_t* float_ws_bytes,
                         size_t* int_ws_bytes);
 
 /*
- * The planner alone, on the host: validate `desc` and write the work-list image
+ * The planner alone, on the host ([POD] "plan 内部做了什么", the host-side part
+ * of plan): validate `desc` and write the work-list image
  * (the exact int32 words pod_plan copies to the device) into `image`, which has
  * room for `image_cap` words. `info` (optional) receives the counts. Returns
  * POD_ERR_WORKSPACE with info->image_ints set if `image` is too small. No device

@@ -235,7 +235,8 @@ def e4m3_to_float(codes) -> np.ndarray:
     (1 + m/8) * 2^(e - 7); only exponent 15 with mantissa 7 is NaN, so the
     largest finite magnitude is 1.75 * 2^8 = 448. This is the FP8 KV-cache
     element type whose calibration scales the POD article's run parameters
-    (q_scale / k_scale / v_scale, "Prefill 侧参数") describe.
+    (q_scale / k_scale / v_scale, "Decode 侧参数与'plan 覆盖'行为")
+    describe.
     """
     b = np.asarray(codes, dtype=np.uint8).astype(np.int64)
     sign = np.where(b >> 7, -1.0, 1.0)
@@ -250,7 +251,7 @@ def attend_rows_fp8_scaled(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np
                            sm_scale: float, q_scale: float, k_scale: float, v_scale: float,
                            sinks: Optional[np.ndarray] = None):
     """Decode attention over an FP8 KV cache with calibration scales (POD
-    article, "Prefill 侧参数": q_scale and k_scale multiply into the decode
+    article, "Decode 侧参数与'plan 覆盖'行为": q_scale and k_scale multiply into the decode
     sm_scale; v_scale multiplies the decode output after the kernel).
 
     k, v hold the decoded FP8 values (float64). Returns O [n, H_qo, D] and the

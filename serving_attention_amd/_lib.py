@@ -9,7 +9,9 @@ import ctypes
 import os
 
 LIB_NAME = "libpod_attn.so"
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+# POD_ATTN_LIB names another build of the same library (the host-only
+# sanitizer build of the planner and ABI layer that the CPU tests use)
+LIB_PATH = os.environ.get("POD_ATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 POD_OK = 0
 POD_ERR_INVALID = 1

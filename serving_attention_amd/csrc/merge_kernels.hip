@@ -42,9 +42,10 @@ struct Vec8<_Float16> {
 
 template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void merge_states_kernel(
-    const T* __restrict__ oa, const float* __restrict__ la, const T* __restrict__ ob,
-    const float* __restrict__ lb, T* oo, float* lo, int64_t n_pairs, int heads,
-    const float* __restrict__ sinks) {
+    // no __restrict__: the outputs may be one of the inputs (each element is
+    // read before it is written, by the same thread)
+    const T* oa, const float* la, const T* ob, const float* lb, T* oo, float* lo, int64_t n_pairs,
+    int heads, const float* __restrict__ sinks) {
   using V = typename Vec8<T>::type;
   const int64_t t = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
   const int64_t pair = t / kLanesPerPair;

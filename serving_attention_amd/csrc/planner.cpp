@@ -451,7 +451,13 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
     if (nt == 0 || nc == 0) chunks_first = false;
     else if (d.order == POD_ORDER_PREFILL_FIRST) chunks_first = false;
     else if (d.order == POD_ORDER_DECODE_FIRST) chunks_first = true;
-    else if (d.order == POD_ORDER_LONGEST_FIRST) chunks_first = items[cl[0]].cost > items[tl[0]].cost;
+    else if (d.order == POD_ORDER_LONGEST_FIRST) {
+      // the list holds each role's tiles heaviest first: compare with the
+      // heavier of the two roles' first tiles
+      int64_t tile_max = 0;
+      for (size_t j = 0; j < nt; ++j) tile_max = std::max(tile_max, items[tl[j]].cost);
+      chunks_first = items[cl[0]].cost > tile_max;
+    }
     else chunks_first = ((w / kNumXcds) & 1) != 0;   // half of each die's workgroups each way
     wg[0] = (int32_t)k;
     wg[1] = (int32_t)nt;

@@ -341,6 +341,17 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     return set_err(POD_ERR_NOT_PLANNED, "plan has sinks: args->sinks is required");
   if (!ctx->has_sinks && args->sinks)
     return set_err(POD_ERR_NOT_PLANNED, "plan has no sinks: args->sinks must be NULL");
+  // the decode role's calibration scales (0 = 1): the online softmax keeps its
+  // running maximum in raw score units and needs a positive, bounded scale
+  if (!std::isfinite(args->q_scale_d) || !std::isfinite(args->k_scale_d) || !std::isfinite(args->v_scale_d))
+    return set_err(POD_ERR_INVALID, "q_scale_d, k_scale_d and v_scale_d must be finite");
+  const auto one = [](float s) { return s == 0.f ? 1.f : s; };
+  const float qk_d = one(args->q_scale_d) * one(args->k_scale_d);
+  if (ctx->role[1].rows > 0) {
+    if (!(qk_d > 0.f)) return set_err(POD_ERR_INVALID, "q_scale_d * k_scale_d must be > 0");
+    if (!(ctx->role[1].sm_scale * qk_d <= 1e6f))
+      return set_err(POD_ERR_INVALID, "sm_scale_d * q_scale_d * k_scale_d must be <= 1e6");
+  }
   pod::Params p{};
   const pod_role_args* ra[2] = {&args->prefill, &args->decode};
   static const char* names[2] = {"prefill", "decode"};
@@ -391,8 +402,7 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     o.lse = a.lse;
     // the decode role's FP8 calibration: q_scale * k_scale fold into the scale,
     // v_scale into the output normalisation (0 = 1)
-    const auto one = [](float s) { return s == 0.f ? 1.f : s; };
-    const float qk = r == 1 ? one(args->q_scale_d) * one(args->k_scale_d) : 1.f;
+    const float qk = r == 1 ? qk_d : 1.f;
     o.scale_log2 = rp.sm_scale * qk * 1.4426950408889634f;
     o.v_scale = r == 1 ? one(args->v_scale_d) : 1.f;
     o.causal = rp.causal;

@@ -128,6 +128,41 @@ class BatchPOD:
                                 int(bool(causal)), int(window_left),
                                 float(sm_scale) if sm_scale is not None else 0.0)
 
+    @classmethod
+    def _plan_desc(cls, qo_indptr_p, kv_indptr_p, last_page_len_p,
+                   qo_indptr_d, kv_indptr_d, last_page_len_d, *,
+                   num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+                   dtype=torch.bfloat16, causal_p: bool = True, causal_d: bool = True,
+                   window_left_p: int = -1, window_left_d: int = -1,
+                   sm_scale_p: Optional[float] = None, sm_scale_d: Optional[float] = None,
+                   sinks: bool = False, decode_chunk: int = 0, order: int = 0,
+                   kv_dtype_d=None, num_cus: int = 0):
+        """The C plan descriptor and the host arrays it points into (kept alive
+        by the caller while the descriptor is used)."""
+        keep = []
+        desc = _lib.PodPlanDesc(
+            cls._role_desc(qo_indptr_p, kv_indptr_p, last_page_len_p, causal_p, window_left_p,
+                           sm_scale_p, keep),
+            cls._role_desc(qo_indptr_d, kv_indptr_d, last_page_len_d, causal_d, window_left_d,
+                           sm_scale_d, keep),
+            int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size),
+            _dtype_code(dtype), int(bool(sinks)), int(num_cus), int(decode_chunk), int(order),
+            _lib.POD_DTYPE_FP8_E4M3 if kv_dtype_d == torch.float8_e4m3fn else 0)
+        if kv_dtype_d not in (None, torch.float8_e4m3fn) and _DT.get(kv_dtype_d) != _dtype_code(dtype):
+            raise NotImplementedError(f"decode K/V dtype {kv_dtype_d} is not supported")
+        return desc, keep
+
+    @classmethod
+    def workspace_bytes(cls, *args, **kwargs) -> Tuple[int, int]:
+        """(float, int) workspace bytes the plan with these arguments (those of
+        plan(), plus ``num_cus``, default 256) needs. Host only."""
+        desc, keep = cls._plan_desc(*args, **kwargs)
+        fb, ib = ctypes.c_size_t(), ctypes.c_size_t()
+        lib = _lib.load()
+        _lib.check(lib.pod_workspace_bytes(ctypes.byref(desc), ctypes.byref(fb), ctypes.byref(ib)))
+        del keep
+        return int(fb.value), int(ib.value)
+
     def plan(self, qo_indptr_p, kv_indptr_p, last_page_len_p,
              qo_indptr_d, kv_indptr_d, last_page_len_d, *,
              num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
@@ -139,20 +174,16 @@ class BatchPOD:
         """Build and upload the work list. Either role may be None (empty).
 
         ``kv_dtype_d=torch.float8_e4m3fn`` plans the decode role over an FP8 KV
-        cache (POD article, "Prefill 侧参数": the calibration scales are decode
+        cache (POD article, "Decode 侧参数与'plan 覆盖'行为": the calibration scales are decode
         run parameters); q and outputs keep ``dtype``.
         """
-        keep = []
-        desc = _lib.PodPlanDesc(
-            self._role_desc(qo_indptr_p, kv_indptr_p, last_page_len_p, causal_p, window_left_p,
-                            sm_scale_p, keep),
-            self._role_desc(qo_indptr_d, kv_indptr_d, last_page_len_d, causal_d, window_left_d,
-                            sm_scale_d, keep),
-            int(num_qo_heads), int(num_kv_heads), int(head_dim), int(page_size),
-            _dtype_code(dtype), int(bool(sinks)), 0, int(decode_chunk), int(order),
-            _lib.POD_DTYPE_FP8_E4M3 if kv_dtype_d == torch.float8_e4m3fn else 0)
-        if kv_dtype_d not in (None, torch.float8_e4m3fn) and _DT.get(kv_dtype_d) != _dtype_code(dtype):
-            raise NotImplementedError(f"decode K/V dtype {kv_dtype_d} is not supported")
+        desc, keep = self._plan_desc(
+            qo_indptr_p, kv_indptr_p, last_page_len_p, qo_indptr_d, kv_indptr_d, last_page_len_d,
+            num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+            page_size=page_size, dtype=dtype, causal_p=causal_p, causal_d=causal_d,
+            window_left_p=window_left_p, window_left_d=window_left_d, sm_scale_p=sm_scale_p,
+            sm_scale_d=sm_scale_d, sinks=sinks, decode_chunk=decode_chunk, order=order,
+            kv_dtype_d=kv_dtype_d)
         s = _stream_handle(self.device) if stream is None else ctypes.c_void_p(stream)
         _lib.check(self._lib.pod_plan(self._ctx, ctypes.byref(desc), s))
         # keep holds (qo, kv, lpl) of each role that is present, prefill first
@@ -209,6 +240,18 @@ class BatchPOD:
                 raise ValueError(f"kv_indices holds {kv_indices.numel()} pages, the plan needs {nnz}")
         elif k.shape[0] < nnz:
             raise ValueError(f"identity page table needs {nnz} pages, the cache has {k.shape[0]}")
+        # outputs: the kernel writes 16-byte vectors of a dense head_dim and the
+        # LSE at row * num_qo_heads + head
+        if not isinstance(out, torch.Tensor) or out.dim() != 3 or out.shape[0] < q.shape[0] \
+                or out.shape[1] != hq or out.shape[2] != d:
+            raise ValueError(f"out must be [{q.shape[0]}, {hq}, {d}]")
+        if out.dtype != q.dtype or out.device != q.device or out.stride(-1) != 1:
+            raise ValueError("out must have q's dtype and device and a dense head_dim")
+        if lse is not None:
+            if lse.dim() != 2 or lse.shape[0] < q.shape[0] or lse.shape[1] != hq:
+                raise ValueError(f"lse must be [{q.shape[0]}, {hq}]")
+            if lse.dtype != torch.float32 or lse.device != q.device or lse.stride() != (hq, 1):
+                raise ValueError("lse must be a contiguous float32 tensor on q's device")
         return _lib.PodRoleArgs(
             q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), v.data_ptr(), sp, st, sh,
             kv_indices.data_ptr() if kv_indices is not None else None,
@@ -223,7 +266,7 @@ class BatchPOD:
         """One fused launch. Returns (out_p, out_d) or ((out_p, lse_p), (out_d, lse_d)).
 
         q_scale_d * k_scale_d multiply the decode sm_scale and v_scale_d the decode
-        output (POD article, "Prefill 侧参数"; here v_scale is folded into the
+        output (POD article, "Decode 侧参数与'plan 覆盖'行为"; here v_scale is folded into the
         launch's final normalisation). None means 1.
         """
         if self._planned is None:
@@ -285,12 +328,17 @@ def single_decode_with_kv_cache(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     if k.stride() != v.stride():
         raise ValueError("k and v must share strides")
     hq = q.shape[0]
+    plan_args = dict(num_qo_heads=hq, num_kv_heads=hk, head_dim=d, page_size=1, dtype=q.dtype,
+                     causal_d=False, window_left_d=window_left, sm_scale_d=sm_scale)
+    dev = q.device.index if q.device.index is not None else torch.cuda.current_device()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    # the workspaces this plan needs (split-KV partial states grow with kv_len)
+    fbytes, ibytes = BatchPOD.workspace_bytes(None, None, None, [0, 1], [0, kv_len], [1],
+                                              num_cus=cus, **plan_args)
     if workspace is None:
-        workspace = torch.empty(16 << 20, dtype=torch.uint8, device=q.device)
-    w = BatchPOD(workspace, "NHD", int_workspace_bytes=1 << 20)
-    w.plan(None, None, None, [0, 1], [0, kv_len], [1],
-           num_qo_heads=hq, num_kv_heads=hk, head_dim=d, page_size=1, dtype=q.dtype,
-           causal_d=False, window_left_d=window_left, sm_scale_d=sm_scale)
+        workspace = torch.empty(max(fbytes, 1 << 16), dtype=torch.uint8, device=q.device)
+    w = BatchPOD(workspace, "NHD", int_workspace_bytes=max(ibytes, 1 << 16))
+    w.plan(None, None, None, [0, 1], [0, kv_len], [1], **plan_args)
     # page_size 1 view: [kv_len, 1, H_kv, D] with the caller's strides
     kp = torch.as_strided(k, (kv_len, 1, hk, d), (sp, sp, sh, 1))
     vp = torch.as_strided(v, (kv_len, 1, hk, d), (sp, sp, sh, 1))

@@ -1,7 +1,7 @@
 """GPU parity of the FP8 (E4M3) decode KV cache against the fp64 oracle.
 
 The decode role reads K/V stored as FP8 E4M3 bytes, with the calibration scales
-of the POD article ("Prefill 侧参数": q_scale * k_scale multiply the decode
+of the POD article ("Decode 侧参数与'plan 覆盖'行为": q_scale * k_scale multiply the decode
 sm_scale, v_scale the decode output); q, the prefill K/V and the outputs keep
 the query dtype. The oracle decodes the stored bytes itself (pinned against
 torch's float8_e4m3fn) and applies the scales by their definition. Tolerances

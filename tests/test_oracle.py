@@ -410,3 +410,163 @@ def test_fp8_scales_fold_into_scale_and_output():
     o3, l3 = oracle.attend_rows_fp8_scaled(q, k, v, keep, 0.09, 1.0, 1.0, 1.0)
     o4, l4 = attend_rows(q, k, v, keep, 0.09)
     assert np.array_equal(o3, o4) and np.array_equal(l3, l4)
+
+
+# ---------------------------------------------------------------- layouts, non-causal rows, brute force
+
+
+def _direct_kv(pool, kv_indptr, kv_indices, kv_len, page_size, b, layout="NHD"):
+    """Keys of request b read straight from the pool with the page-table rule
+    (logical key j = physical page kv_indices[kv_indptr[b] + j // page_size],
+    slot j % page_size), one key at a time: [kv_len, H_kv, D]."""
+    rows = []
+    for j in range(kv_len):
+        page = int(kv_indices[int(kv_indptr[b]) + j // page_size])
+        slot = j % page_size
+        rows.append(pool[page, slot] if layout == "NHD" else pool[page, :, slot])
+    return np.stack(rows).astype(np.float64)
+
+
+@pytest.mark.parametrize("ps,hkv", [(3, 2), (2, 2), (5, 1)])
+def test_hnd_layout_equals_nhd(ps, hkv):
+    """The same pool stored head-major ([P, H_kv, page_size, D]) gives the
+    identical result; page_size == H_kv is included, where an index mix-up of
+    the two axes keeps the shapes."""
+    rng = np.random.default_rng(30 + ps)
+    inp = paged_inputs(rng, [17, 6], [4, 6], ps, 2 * hkv, hkv, 8)
+    a = run(inp, causal=True, window_left=5)
+    hnd = dict(inp, k_pool=np.ascontiguousarray(inp["k_pool"].transpose(0, 2, 1, 3)),
+               v_pool=np.ascontiguousarray(inp["v_pool"].transpose(0, 2, 1, 3)), layout="HND")
+    b = run(hnd, causal=True, window_left=5)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
+    # and the head-major keys themselves, read key by key from the pool
+    kv_len = int(oracle.seq_lens(inp["kv_indptr"], inp["last_page_len"], ps)[0])
+    k, _ = oracle.logical_kv(hnd["k_pool"], hnd["v_pool"], inp["kv_indptr"], inp["kv_indices"],
+                             inp["last_page_len"], ps, 0, layout="HND")
+    np.testing.assert_array_equal(k, _direct_kv(hnd["k_pool"], inp["kv_indptr"], inp["kv_indices"],
+                                                kv_len, ps, 0, layout="HND"))
+
+
+@pytest.mark.parametrize("hqo,hkv", [(4, 4), (6, 2)])
+def test_non_causal_multi_row_matches_torch_sdpa(hqo, hkv):
+    """Without the causal mask every row of a q_len < kv_len request sees every
+    key: torch SDPA (fp64, no mask, enable_gqa) over keys read straight from the
+    pool."""
+    rng = np.random.default_rng(40 + hqo)
+    kv, ql, d, scale = 29, 7, 16, 0.27
+    inp = paged_inputs(rng, [kv], [ql], 4, hqo, hkv, d)
+    o, lse = run(inp, causal=False, sm_scale=scale)
+    k = _direct_kv(inp["k_pool"], inp["kv_indptr"], inp["kv_indices"], kv, 4, 0)
+    v = _direct_kv(inp["v_pool"], inp["kv_indptr"], inp["kv_indices"], kv, 4, 0)
+    qt = torch.from_numpy(inp["q"]).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2)[None]
+    ref = F.scaled_dot_product_attention(qt, kt, vt, is_causal=False, scale=scale, enable_gqa=True)
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    # every row's lse is the log-sum-exp over all kv keys
+    g = hqo // hkv
+    for i in range(ql):
+        for h in range(hqo):
+            s = scale * (k[:, h // g] @ inp["q"][i, h])
+            assert abs(lse[i, h] - scipy.special.logsumexp(s) / math.log(2)) < 1e-12
+
+
+def test_window_without_causal_matches_enumeration():
+    """Window without the causal mask: row i sees keys p_i - window_left ..
+    kv_len - 1 (clipped at 0), p_i = kv_len - q_len + i."""
+    for kv in range(1, 13):
+        for ql in range(1, kv + 1):
+            for w in (0, 1, 2, 5, 30):
+                m = valid_key_mask(ql, kv, False, w)
+                for i in range(ql):
+                    diag = kv - ql + i
+                    allowed = set(range(max(0, diag - w), kv))
+                    assert set(np.nonzero(m[i])[0].tolist()) == allowed
+    # and the attention itself over those keys
+    rng = np.random.default_rng(43)
+    kv, ql, w = 19, 6, 4
+    inp = paged_inputs(rng, [kv], [ql], 3, 2, 1, 8)
+    o, lse = run(inp, causal=False, window_left=w, sm_scale=0.5)
+    k = _direct_kv(inp["k_pool"], inp["kv_indptr"], inp["kv_indices"], kv, 3, 0)
+    v = _direct_kv(inp["v_pool"], inp["kv_indptr"], inp["kv_indices"], kv, 3, 0)
+    for i in range(ql):
+        J = list(range(max(0, kv - ql + i - w), kv))
+        for h in range(2):
+            s = 0.5 * (k[J, 0] @ inp["q"][i, h])
+            p = scipy.special.softmax(s)
+            np.testing.assert_allclose(o[i, h], p @ v[J, 0], atol=1e-12)
+            assert abs(lse[i, h] - scipy.special.logsumexp(s) / math.log(2)) < 1e-12
+
+
+def _brute_force(inp, causal, window_left, sm_scale, sinks=None):
+    """Scalar pure-Python evaluation of the definition: each key read from the
+    pool by the page-table rule, every sum taken with math.fsum."""
+    q, kp, vp = inp["q"], inp["k_pool"], inp["v_pool"]
+    ps, hqo, hkv = inp["page_size"], inp["num_qo_heads"], inp["num_kv_heads"]
+    g = hqo // hkv
+    d = q.shape[-1]
+    out = np.zeros_like(q)
+    lse = np.zeros(q.shape[:2])
+    nreq = len(inp["qo_indptr"]) - 1
+    for b in range(nreq):
+        npages = int(inp["kv_indptr"][b + 1] - inp["kv_indptr"][b])
+        kv_len = (npages - 1) * ps + int(inp["last_page_len"][b])
+        q0, q1 = int(inp["qo_indptr"][b]), int(inp["qo_indptr"][b + 1])
+        ql = q1 - q0
+        for i in range(ql):
+            diag = kv_len - ql + i
+            for h in range(hqo):
+                kh = h // g
+                keys = [j for j in range(kv_len)
+                        if (not causal or j <= diag) and (window_left < 0 or j >= diag - window_left)]
+                s = {}
+                for j in keys:
+                    page = int(inp["kv_indices"][int(inp["kv_indptr"][b]) + j // ps])
+                    kvec = kp[page, j % ps, kh]
+                    s[j] = sm_scale * math.fsum(float(q[q0 + i, h, t]) * float(kvec[t]) for t in range(d))
+                m = max(s.values())
+                e = {j: math.exp(s[j] - m) for j in keys}
+                z = math.fsum(e.values())
+                den = z + (math.exp(float(sinks[h]) - m) if sinks is not None else 0.0)
+                for t in range(d):
+                    num = math.fsum(e[j] * float(vp[int(inp["kv_indices"][int(inp["kv_indptr"][b]) + j // ps]),
+                                                    j % ps, kh, t]) for j in keys)
+                    out[q0 + i, h, t] = num / den
+                lse[q0 + i, h] = (m + math.log(z)) / math.log(2.0)
+    return out, lse
+
+
+@pytest.mark.parametrize("causal,w,with_sinks", [(True, -1, False), (True, 3, True), (False, -1, False),
+                                                  (False, 2, True)])
+def test_scalar_brute_force(causal, w, with_sinks):
+    """The oracle equals a scalar evaluation that reads every key from the pool
+    directly (no shared helper), to 1e-12: paging, GQA, mask, scale, sinks and
+    the base-2 lse together."""
+    rng = np.random.default_rng(50 + int(causal) + 2 * (w + 1))
+    inp = paged_inputs(rng, [11, 5, 8], [3, 5, 1], 3, 4, 2, 6)
+    sinks = rng.standard_normal(4) if with_sinks else None
+    o, lse = run(inp, causal=causal, window_left=w, sm_scale=0.45, sinks=sinks)
+    bo, bl = _brute_force(inp, causal, w, 0.45, sinks)
+    np.testing.assert_allclose(o, bo, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=0, atol=1e-12)
+
+
+def test_dropping_pages_before_the_window_changes_nothing():
+    """Keys outside every row's window weigh exactly zero: dropping the whole
+    leading pages before the request's earliest visible key (and shortening
+    kv_len by as much, which keeps each row's diagonal on the same key) gives
+    the identical result. The GPU parity tests use this to bring long windowed
+    requests to the host."""
+    rng = np.random.default_rng(60)
+    ps, kv, ql, w = 4, 57, 5, 9
+    inp = paged_inputs(rng, [kv], [ql], ps, 4, 2, 8)
+    for causal in (True, False):
+        a = run(inp, causal=causal, window_left=w)
+        lo = kv - ql - w                       # earliest visible key of row 0
+        drop = lo // ps
+        cut = dict(inp, kv_indices=inp["kv_indices"][drop:],
+                   kv_indptr=np.array([0, int(inp["kv_indptr"][1]) - drop]))
+        b = run(cut, causal=causal, window_left=w)
+        np.testing.assert_array_equal(a[0], b[0])
+        np.testing.assert_array_equal(a[1], b[1])

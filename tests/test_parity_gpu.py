@@ -202,6 +202,31 @@ def test_single_decode_api_matches_oracle():
         assert eo <= TOL_O["f16"] and el <= TOL_LSE
 
 
+@pytest.mark.parametrize("hq,hk,kv_len", [(64, 8, 32768), (32, 32, 32768), (8, 8, 65536), (8, 1, 262144)])
+def test_single_decode_long_context(hq, hk, kv_len):
+    """Long single-request decodes through single_decode_with_kv_cache: the
+    split-KV partial states of these plans need more than 16 MiB of float
+    workspace, which the call sizes from the plan itself."""
+    log(f"case: single decode {hq}/{hk} heads, {kv_len} keys (bf16)")
+    fbytes, _ = BatchPOD.workspace_bytes(None, None, None, [0, 1], [0, kv_len], [1], num_qo_heads=hq,
+                                         num_kv_heads=hk, head_dim=128, page_size=1, causal_d=False,
+                                         num_cus=torch.cuda.get_device_properties(0).multi_processor_count)
+    log(f"float workspace needed: {fbytes} bytes")
+    g = torch.Generator(device="cuda").manual_seed(kv_len + hq)
+    q = torch.randn(hq, 128, generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn(kv_len, hk, 128, generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn(kv_len, hk, 128, generator=g, device="cuda").to(torch.bfloat16)
+    o, lse = single_decode_with_kv_cache(q, k, v, return_lse=True)
+    torch.cuda.synchronize()
+    import oracle
+    ro, rl = oracle.attend_rows(q.float().cpu().numpy()[None], k.float().cpu().numpy(),
+                                v.float().cpu().numpy(), np.ones((1, kv_len), bool), 128 ** -0.5)
+    eo = float(np.abs(o.float().cpu().numpy() - ro[0]).max())
+    el = float(np.abs(lse.cpu().numpy() - rl[0]).max())
+    log(f"single_decode long: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O["bf16"] and el <= TOL_LSE
+
+
 def test_run_errors():
     log("case: run-time error paths")
     w = build(small_spec(p_q=(10,), p_kv=(10,), d_kv=(20,), hqo=8, hkv=2), device="cuda")
@@ -220,6 +245,28 @@ def test_run_errors():
     with pytest.raises(ValueError):
         pod.run(w.prefill.q[:5], w.prefill.kv_cache, w.prefill.kv_indices_dev,
                 w.decode.q, w.decode.kv_cache, w.decode.kv_indices_dev)
+    # caller-supplied outputs are checked like q: rows, heads, dtype, dense head_dim,
+    # and a contiguous fp32 LSE (the kernel writes lse[row * num_qo_heads + head])
+    args = (w.prefill.q, w.prefill.kv_cache, w.prefill.kv_indices_dev,
+            w.decode.q, w.decode.kv_cache, w.decode.kv_indices_dev)
+    qp = w.prefill.q
+    bad_outs = [
+        dict(out_p=torch.empty(5, 8, 128, dtype=qp.dtype, device="cuda")),
+        dict(out_p=torch.empty(10, 8, 128, dtype=torch.float16, device="cuda")),
+        dict(out_p=torch.empty(10, 8, 256, dtype=qp.dtype, device="cuda")[:, :, ::2]),
+        dict(out_d=torch.empty(1, 4, 128, dtype=qp.dtype, device="cuda")),
+        dict(lse_p=torch.empty(10, 16, device="cuda")[:, :8], return_lse=True),
+        dict(lse_p=torch.empty(10, 8, dtype=torch.float16, device="cuda"), return_lse=True),
+        dict(lse_d=torch.empty(0, 8, device="cuda"), return_lse=True),
+    ]
+    for kw in bad_outs:
+        with pytest.raises(ValueError):
+            pod.run(*args, **kw)
+    # the decode scales: finite, q_scale * k_scale > 0, effective scale <= 1e6
+    for kw in (dict(q_scale_d=-1.0), dict(k_scale_d=float("nan")), dict(v_scale_d=float("inf")),
+               dict(q_scale_d=1e4, k_scale_d=1e4)):
+        with pytest.raises(ValueError):
+            pod.run(*args, **kw)
     # workspace too small for a split plan: one request of 2000 keys in chunks of 64
     tiny = BatchPOD(torch.empty(4096, dtype=torch.uint8, device="cuda"))
     with pytest.raises(_lib.PodError):

@@ -177,6 +177,11 @@ WORKLOADS = [
          decode=dict(qo_lens=[4] * 64, kv_lens=[1024 + 500 * i for i in range(64)], window_left=4096),
          hqo=64, hkv=8),
     dict(decode=dict(qo_lens=[1, 2], kv_lens=[100, 300]), hqo=64, hkv=1),
+    # group 16: one-token decodes are key chunks, three-token decodes (48 rows)
+    # query tiles, some of them heavier than the prefill tiles
+    dict(prefill=dict(qo_lens=[40, 90], kv_lens=[200, 90]),
+         decode=dict(qo_lens=[1, 3, 1, 3, 2, 3] * 6, kv_lens=[300, 3000, 900, 500, 4000, 2500] * 6),
+         hqo=32, hkv=2),
 ]
 
 
@@ -213,7 +218,7 @@ def test_workgroup_lists(wl, order):
         loads[w] = sum(item_cost(it) for it in items[first:first + nt + nc])
         if nt and nc:
             expect = {0: (w // 8) % 2 == 1, 1: False, 2: True,
-                      3: item_cost(chunks[0]) > item_cost(tiles[0])}[order]
+                      3: item_cost(chunks[0]) > max(item_cost(t) for t in tiles)}[order]
             assert bool(chunks_first) == expect
         else:
             assert chunks_first == 0
@@ -325,3 +330,21 @@ def test_invalid_page_tables(role):
     rc, _, _ = compute(desc)
     assert rc == _lib.POD_ERR_INVALID
     assert _lib.load().pod_last_error()
+
+
+@pytest.mark.parametrize("hq,hk,kv_len", [(64, 8, 32768), (32, 32, 32768), (8, 8, 65536), (8, 1, 262144)])
+def test_workspace_query_of_long_single_decodes(hq, hk, kv_len):
+    """The float workspace a plan needs is its split slots times one partial
+    state (32 rows x 128 O + 32 LSE, fp32); long single decodes need more than
+    the 16 MiB the single-decode call once allocated, and the binding's query
+    reports the same sizes as the planner."""
+    from serving_attention_amd import BatchPOD
+    kw = dict(num_qo_heads=hq, num_kv_heads=hk, head_dim=128, page_size=1, causal_d=False, num_cus=256)
+    fb, ib = BatchPOD.workspace_bytes(None, None, None, [0, 1], [0, kv_len], [1], **kw)
+    desc, keep = plan_desc(decode=dict(qo_lens=[1], kv_lens=[kv_len], causal=False), hqo=hq, hkv=hk,
+                           page_size=1)
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    assert fb == info.float_ws_bytes == info.n_slots * (32 * 128 + 32) * 4
+    assert ib == info.int_ws_bytes
+    assert info.n_groups > 0 and fb > 16 << 20
