@@ -261,7 +261,10 @@ int pod_destroy(pod_ctx_t ctx);
  *   waits for them only if they are still running), so it overlaps the
  *   previous plan's launches; pod_plan then waits on the host for that copy
  *   alone (a few microseconds), so pod_run needs no stream-ordering of its own.
- *   `stream` is not used in this mode.
+ *   The first copy into each half is also ordered after the work queued on
+ *   `stream` when pod_plan is called (so a caller that initialises int_ws on
+ *   `stream` just before, or still uses that memory there, is safe); pod_plan
+ *   then waits for that work too. `stream` serves only this in this mode.
  *   Graph context (pod_create_graph): the copy is enqueued on `stream`, ahead of
  *   the launches that follow there; pod_plan does not wait for it.
  * Errors: POD_ERR_INVALID / POD_ERR_UNSUPPORTED for descriptors the planner

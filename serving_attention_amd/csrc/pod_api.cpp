@@ -58,6 +58,11 @@ struct pod_ctx {
   hipEvent_t used[2] = {nullptr, nullptr};     // last launch that read half k done
   bool used_pending[2] = {false, false};
   hipStream_t copy_stream = nullptr;
+  // The first copy into each half waits for the work the caller had queued on
+  // its stream by then (its initialisation of the workspace, say); later
+  // copies into a half are ordered by the launches that last read it.
+  hipEvent_t caller_ready = nullptr;
+  bool half_ordered[2] = {false, false};
   int next_staging = 0;
   int cur = 0;                                 // half of the current plan
   // Graph mode (pod_create_graph): fixed batch sizes, one image at the start of
@@ -180,6 +185,7 @@ int pod_destroy(pod_ctx_t ctx) {
       }
       if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
     }
+    if (ctx->caller_ready) (void)hipEventDestroy(ctx->caller_ready);
     if (ctx->copy_stream) (void)hipStreamDestroy(ctx->copy_stream);
   }
   delete ctx;
@@ -288,6 +294,17 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
     e = hipEventSynchronize(ctx->used[k]);
     if (e != hipSuccess) return hip_err(e, "hipEventSynchronize");
     ctx->used_pending[k] = false;
+  }
+  if (!ctx->half_ordered[k]) {
+    if (!ctx->caller_ready) {
+      e = hipEventCreateWithFlags(&ctx->caller_ready, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_err(e, "hipEventCreate");
+    }
+    e = hipEventRecord(ctx->caller_ready, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_err(e, "hipEventRecord (caller stream)");
+    e = hipStreamWaitEvent(ctx->copy_stream, ctx->caller_ready, 0);
+    if (e != hipSuccess) return hip_err(e, "hipStreamWaitEvent");
+    ctx->half_ordered[k] = true;
   }
   e = hipMemcpyAsync(int_half(ctx, k), ctx->staging[k], bytes, hipMemcpyHostToDevice, ctx->copy_stream);
   if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (work list)");

@@ -70,9 +70,20 @@ def oracle_request(w, role, b, rows=None):
     """fp64 oracle for request b of a role (optionally some of its rows).
 
     Copies only the request's own pages to the host and renumbers them, which
-    leaves the result unchanged (page-permutation invariance of the oracle)."""
+    leaves the result unchanged (page-permutation invariance of the oracle).
+    With a window it also leaves out the whole pages before the earliest key
+    any of the rows sees, shortening kv_len by as much: each row keeps its
+    diagonal key, and the dropped keys weigh exactly zero (pinned on the CPU
+    by the oracle tests)."""
     spec = w.spec
     p0, p1 = int(role.kv_indptr[b]), int(role.kv_indptr[b + 1])
+    q0, q1 = int(role.qo_indptr[b]), int(role.qo_indptr[b + 1])
+    if role.window_left >= 0 and q1 > q0:
+        kv_len = (p1 - p0 - 1) * spec.page_size + int(role.last_page_len[b])
+        # earliest key of the request's first row (kv_len' >= q_len + window_left
+        # stays, so every row keeps its whole window)
+        lo = max(0, kv_len - (q1 - q0) - role.window_left)
+        p0 += min(lo // spec.page_size, p1 - p0 - 1)
     pages = torch.from_numpy(role.kv_indices[p0:p1].astype(np.int64)).to(role.k_pool.device)
     fp8 = role is w.decode and spec.decode_kv_dtype == "fp8_e4m3"
     qs, ks, vs = spec.fp8_scales if fp8 else (1.0, 1.0, 1.0)
@@ -82,7 +93,6 @@ def oracle_request(w, role, b, rows=None):
     else:
         kp = role.k_pool.index_select(0, pages).float().cpu().numpy()
         vp = role.v_pool.index_select(0, pages).float().cpu().numpy()
-    q0, q1 = int(role.qo_indptr[b]), int(role.qo_indptr[b + 1])
     q = role.q[q0:q1].float().cpu().numpy()
     sinks = w.sinks.cpu().numpy() if spec.sinks else None
     res = oracle.attend_role(

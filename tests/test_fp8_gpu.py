@@ -95,7 +95,11 @@ def test_named_pod_fp8():
     res, pod = plan_and_run(w)
     (op, lp), (od, ld) = res
     rng = np.random.default_rng(9)
-    reqs = sorted(set(rng.choice(128, 32, replace=False).tolist()))
-    assert_close(w, compare_role(w, w.decode, od, ld, requests=reqs, tag="pod_fp8/decode"), "pod_fp8/decode")
+    # the bf16 prefill role on sampled rows (tile edges plus random rows), every
+    # FP8 decode request
+    rows = lambda b: np.array(sorted({0, 1, 31, 32, 63, 64, 1023, 1024, 2046, 2047} |
+                                     set(rng.integers(0, 2048, 30).tolist())))
+    assert_close(w, compare_role(w, w.prefill, op, lp, rows_of=rows, tag="pod_fp8/prefill"), "pod_fp8/prefill")
+    assert_close(w, compare_role(w, w.decode, od, ld, tag="pod_fp8/decode"), "pod_fp8/decode")
     del w
     torch.cuda.empty_cache()
