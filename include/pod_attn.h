@@ -355,6 +355,31 @@ int pod_plan_compute(const pod_plan_desc* desc, int32_t* image, size_t image_cap
                      pod_plan_info* info);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): pod_plan and
+ * pod_run in one call, with no context and no workspaces. The work list and the
+ * split-KV partial states live in the library's static device scratch (64 MiB
+ * per device, held until the process ends: a 16 MiB work list and 48 MiB of
+ * partial states, about 2,900 split chunks of 32 rows); plans that need more
+ * are refused with POD_ERR_WORKSPACE before anything is enqueued.
+ *   desc, args  as for pod_plan and pod_run (num_cus 0 asks `device`); the
+ *               host arrays of desc are read during the call only.
+ *   device      the HIP device whose scratch is used; made current for the
+ *               call and restored after.
+ *   stream      the work list is copied from host memory on `stream`, then
+ *               the fused grid is launched there. The copy is from memory that
+ *               is not pinned, so the call may wait on the host for work
+ *               already queued on `stream`.
+ * Calls no hipMalloc, hipHostMalloc or hipFree (the host planner's working
+ * memory comes from the C++ heap). Every call on a device shares that device's
+ * scratch and the library's host image buffer: calls are serialised on the
+ * host, and calls whose launches can overlap on one device (different streams
+ * without ordering between them) race on the scratch. Errors as pod_plan and
+ * pod_run, plus POD_ERR_WORKSPACE for plans above the static limits.
+ */
+int pod_run_static(const pod_plan_desc* desc, const pod_run_args* args, int device, void* stream);
+
+/*
  * Work-list image layout (int32 words), for inspection by tools and tests.
  *   header[POD_HDR_WORDS]: [0] magic POD_IMAGE_MAGIC, [1] n_items, [2] grid,
  *     [3] n_reqs, [4] n_groups, [5] reqs_off, [6] items_off, [7] groups_off,

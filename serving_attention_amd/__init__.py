@@ -3,7 +3,7 @@
 The compute path is the HIP library ``libpod_attn.so`` (built in-tree from
 ``csrc/``); this package only marshals arguments to its C ABI.
 """
-from .pod import BatchPOD, single_decode_with_kv_cache, kv_views, merge_states  # noqa: F401
+from .pod import BatchPOD, single_decode_with_kv_cache, kv_views, merge_states, run_static  # noqa: F401
 from . import _lib  # noqa: F401
 
-__all__ = ["BatchPOD", "single_decode_with_kv_cache", "kv_views", "merge_states"]
+__all__ = ["BatchPOD", "single_decode_with_kv_cache", "kv_views", "merge_states", "run_static"]

@@ -35,7 +35,7 @@ POD_IMAGE_MAGIC = 0x504F4431
 EXPORTED = (
     "pod_create", "pod_destroy", "pod_plan", "pod_plan_stats", "pod_run",
     "pod_last_error", "pod_workspace_bytes", "pod_plan_compute", "pod_merge_states",
-    "pod_create_graph",
+    "pod_create_graph", "pod_run_static",
 )
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
@@ -148,8 +148,10 @@ def load() -> ctypes.CDLL:
     fp = ctypes.POINTER(ctypes.c_float)
     lib.pod_merge_states.argtypes = [vp, fp, vp, fp, vp, fp, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, fp, ctypes.c_int, vp]
+    lib.pod_run_static.argtypes = [ctypes.POINTER(PodPlanDesc), ctypes.POINTER(PodRunArgs), ctypes.c_int, vp]
     for name in ("pod_create", "pod_destroy", "pod_plan", "pod_plan_stats", "pod_run",
-                 "pod_workspace_bytes", "pod_plan_compute", "pod_merge_states", "pod_create_graph"):
+                 "pod_workspace_bytes", "pod_plan_compute", "pod_merge_states", "pod_create_graph",
+                 "pod_run_static"):
         getattr(lib, name).restype = ctypes.c_int
     _LIB = lib
     return lib

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -33,6 +34,45 @@ struct RolePlan {
   float sm_scale = 0.f;
 };
 
+// What a plan fixes for the runs that use it (besides the work list itself).
+struct PlanShape {
+  RolePlan role[2];
+  int32_t num_qo_heads = 0, num_kv_heads = 0, page_size = 0, dtype = 0, has_sinks = 0;
+  bool decode_kv_fp8 = false;
+};
+
+// The shape of a validated plan descriptor.
+void plan_shape(const pod_plan_desc& d, PlanShape& s) {
+  const pod_role_desc* rd[2] = {&d.prefill, &d.decode};
+  for (int r = 0; r < 2; ++r) {
+    RolePlan& rp = s.role[r];
+    rp.batch = rd[r]->batch;
+    rp.rows = rd[r]->batch > 0 ? rd[r]->qo_indptr[rd[r]->batch] : 0;
+    rp.causal = rd[r]->causal ? 1 : 0;
+    rp.window_left = rd[r]->window_left;
+    rp.sm_scale = rd[r]->sm_scale > 0.f ? rd[r]->sm_scale : 1.0f / std::sqrt((float)d.head_dim);
+  }
+  s.num_qo_heads = d.num_qo_heads;
+  s.num_kv_heads = d.num_kv_heads;
+  s.page_size = d.page_size;
+  s.dtype = d.dtype;
+  s.has_sinks = d.has_sinks ? 1 : 0;
+  s.decode_kv_fp8 = d.decode_kv_dtype == POD_DTYPE_FP8_E4M3;
+}
+
+// Check the run arguments against the plan's shape and fill the launch
+// parameters (all but the work-list image and the partial-state buffer).
+int fill_params(const PlanShape& sh, const pod_run_args* args, pod::Params& p);
+
+}  // namespace
+
+namespace {
+
+// pod_run_static: the work list is written here on the host and copied into
+// the device's static scratch array; one call at a time.
+std::mutex g_static_mu;
+int32_t g_static_image[pod::kStaticImageBytes / sizeof(int32_t)];
+
 }  // namespace
 
 struct pod_ctx {
@@ -43,9 +83,7 @@ struct pod_ctx {
   size_t int_bytes = 0;
   int num_cus = 0;
   bool planned = false;
-  RolePlan role[2];
-  int32_t num_qo_heads = 0, num_kv_heads = 0, page_size = 0, dtype = 0, has_sinks = 0;
-  bool decode_kv_fp8 = false;
+  PlanShape shape;
   pod_plan_info info{};
   int32_t hdr[POD_HDR_WORDS] = {};
   // Plans alternate between two halves of the int workspace, each with a
@@ -94,6 +132,93 @@ struct DeviceGuard {
     if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
   }
 };
+
+}  // namespace
+
+namespace {
+
+int fill_params(const PlanShape& sh, const pod_run_args* args, pod::Params& p) {
+  if (sh.has_sinks && !args->sinks)
+    return set_err(POD_ERR_NOT_PLANNED, "plan has sinks: args->sinks is required");
+  if (!sh.has_sinks && args->sinks)
+    return set_err(POD_ERR_NOT_PLANNED, "plan has no sinks: args->sinks must be NULL");
+  // the decode role's calibration scales (0 = 1): the online softmax keeps its
+  // running maximum in raw score units and needs a positive, bounded scale
+  if (!std::isfinite(args->q_scale_d) || !std::isfinite(args->k_scale_d) || !std::isfinite(args->v_scale_d))
+    return set_err(POD_ERR_INVALID, "q_scale_d, k_scale_d and v_scale_d must be finite");
+  const auto one = [](float s) { return s == 0.f ? 1.f : s; };
+  const float qk_d = one(args->q_scale_d) * one(args->k_scale_d);
+  if (sh.role[1].rows > 0) {
+    if (!(qk_d > 0.f)) return set_err(POD_ERR_INVALID, "q_scale_d * k_scale_d must be > 0");
+    if (!(sh.role[1].sm_scale * qk_d <= 1e6f))
+      return set_err(POD_ERR_INVALID, "sm_scale_d * q_scale_d * k_scale_d must be <= 1e6");
+  }
+  p = pod::Params{};
+  const pod_role_args* ra[2] = {&args->prefill, &args->decode};
+  static const char* names[2] = {"prefill", "decode"};
+  for (int r = 0; r < 2; ++r) {
+    const RolePlan& rp = sh.role[r];
+    const pod_role_args& a = *ra[r];
+    pod::RoleParams& o = p.role[r];
+    const bool fp8 = r == 1 && sh.decode_kv_fp8;
+    const int esz = fp8 ? 1 : 2;   // bytes per K/V element
+    if (rp.rows > 0) {
+      if (!a.q || !a.k_cache || !a.v_cache || !a.out)
+        return set_err(POD_ERR_INVALID, std::string(names[r]) + ": q, k_cache, v_cache and out are required");
+      if (a.q_stride_tok <= 0 || a.q_stride_head <= 0 || a.kv_stride_page <= 0 ||
+          a.kv_stride_tok <= 0 || a.kv_stride_head <= 0 || a.out_stride_tok <= 0 ||
+          a.out_stride_head <= 0)
+        return set_err(POD_ERR_INVALID, std::string(names[r]) + ": strides must be positive");
+      const uintptr_t mis = reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k_cache) |
+                            reinterpret_cast<uintptr_t>(a.v_cache) | reinterpret_cast<uintptr_t>(a.out);
+      const int64_t smis = a.q_stride_tok | a.q_stride_head | a.kv_stride_page | a.kv_stride_tok |
+                           a.kv_stride_head | a.out_stride_tok | a.out_stride_head;
+      if ((mis & 15) || (smis & 7))
+        return set_err(POD_ERR_INVALID, std::string(names[r]) +
+                                             ": buffers must be 16-byte aligned and strides multiples of 8 elements");
+      if (fp8 && ((a.kv_stride_page | a.kv_stride_tok | a.kv_stride_head) & 15))
+        return set_err(POD_ERR_INVALID, "decode: FP8 K/V strides must be multiples of 16 elements");
+      if (fp8 && !a.kv_indices)
+        return set_err(POD_ERR_INVALID, "decode: FP8 K/V needs kv_indices (no identity page table)");
+      const int64_t lim = (int64_t)1 << 30;   // bytes = 2 * elements must stay below 2^31
+      if (a.kv_stride_page >= lim || a.kv_stride_tok >= lim || a.kv_stride_head >= lim)
+        return set_err(POD_ERR_UNSUPPORTED, std::string(names[r]) +
+                                                ": KV pool strides must be below 2^30 elements");
+      if (a.lse && (reinterpret_cast<uintptr_t>(a.lse) & 3))
+        return set_err(POD_ERR_INVALID, std::string(names[r]) + ": lse must be 4-byte aligned");
+    }
+    o.q = a.q;
+    o.q_st = a.q_stride_tok;
+    o.q_sh = a.q_stride_head;
+    o.k = a.k_cache;
+    o.v = a.v_cache;
+    o.kv_sp_b = (uint32_t)(a.kv_stride_page * esz);
+    o.kv_st_b = (uint32_t)(a.kv_stride_tok * esz);
+    o.kv_sh_b = (uint32_t)(a.kv_stride_head * esz);
+    o.kv_fp8 = fp8 ? 1 : 0;
+    o.indices = a.kv_indices;
+    o.out = a.out;
+    o.o_st = a.out_stride_tok;
+    o.o_sh = a.out_stride_head;
+    o.lse = a.lse;
+    // the decode role's FP8 calibration: q_scale * k_scale fold into the scale,
+    // v_scale into the output normalisation (0 = 1)
+    const float qk = r == 1 ? qk_d : 1.f;
+    o.scale_log2 = rp.sm_scale * qk * 1.4426950408889634f;
+    o.v_scale = r == 1 ? one(args->v_scale_d) : 1.f;
+    o.causal = rp.causal;
+    o.window_left = rp.window_left;
+  }
+  p.sinks = args->sinks;
+  p.num_qo_heads = sh.num_qo_heads;
+  p.num_kv_heads = sh.num_kv_heads;
+  p.group_size = sh.num_qo_heads / sh.num_kv_heads;
+  p.page_size = sh.page_size;
+  p.page_shift = -1;
+  for (int b = 0; b < 31; ++b)
+    if ((1 << b) == sh.page_size) p.page_shift = b;
+  return POD_OK;
+}
 
 }  // namespace
 
@@ -321,21 +446,7 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   ctx->next_staging = 1 - k;
   }
 
-  const pod_role_desc* rd[2] = {&d.prefill, &d.decode};
-  for (int r = 0; r < 2; ++r) {
-    RolePlan& rp = ctx->role[r];
-    rp.batch = rd[r]->batch;
-    rp.rows = rd[r]->batch > 0 ? rd[r]->qo_indptr[rd[r]->batch] : 0;
-    rp.causal = rd[r]->causal ? 1 : 0;
-    rp.window_left = rd[r]->window_left;
-    rp.sm_scale = rd[r]->sm_scale > 0.f ? rd[r]->sm_scale : 1.0f / std::sqrt((float)d.head_dim);
-  }
-  ctx->num_qo_heads = d.num_qo_heads;
-  ctx->num_kv_heads = d.num_kv_heads;
-  ctx->page_size = d.page_size;
-  ctx->dtype = d.dtype;
-  ctx->has_sinks = d.has_sinks ? 1 : 0;
-  ctx->decode_kv_fp8 = d.decode_kv_dtype == POD_DTYPE_FP8_E4M3;
+  plan_shape(d, ctx->shape);
   ctx->info = inf;
   memcpy(ctx->hdr, ctx->staging[k], sizeof(ctx->hdr));
   ctx->planned = true;
@@ -354,94 +465,18 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
   if (!ctx) return set_err(POD_ERR_INVALID, "ctx is NULL");
   if (!args) return set_err(POD_ERR_INVALID, "args is NULL");
   if (!ctx->planned) return set_err(POD_ERR_NOT_PLANNED, "pod_run called before pod_plan");
-  if (ctx->has_sinks && !args->sinks)
-    return set_err(POD_ERR_NOT_PLANNED, "plan has sinks: args->sinks is required");
-  if (!ctx->has_sinks && args->sinks)
-    return set_err(POD_ERR_NOT_PLANNED, "plan has no sinks: args->sinks must be NULL");
-  // the decode role's calibration scales (0 = 1): the online softmax keeps its
-  // running maximum in raw score units and needs a positive, bounded scale
-  if (!std::isfinite(args->q_scale_d) || !std::isfinite(args->k_scale_d) || !std::isfinite(args->v_scale_d))
-    return set_err(POD_ERR_INVALID, "q_scale_d, k_scale_d and v_scale_d must be finite");
-  const auto one = [](float s) { return s == 0.f ? 1.f : s; };
-  const float qk_d = one(args->q_scale_d) * one(args->k_scale_d);
-  if (ctx->role[1].rows > 0) {
-    if (!(qk_d > 0.f)) return set_err(POD_ERR_INVALID, "q_scale_d * k_scale_d must be > 0");
-    if (!(ctx->role[1].sm_scale * qk_d <= 1e6f))
-      return set_err(POD_ERR_INVALID, "sm_scale_d * q_scale_d * k_scale_d must be <= 1e6");
-  }
   pod::Params p{};
-  const pod_role_args* ra[2] = {&args->prefill, &args->decode};
-  static const char* names[2] = {"prefill", "decode"};
-  for (int r = 0; r < 2; ++r) {
-    const RolePlan& rp = ctx->role[r];
-    const pod_role_args& a = *ra[r];
-    pod::RoleParams& o = p.role[r];
-    const bool fp8 = r == 1 && ctx->decode_kv_fp8;
-    const int esz = fp8 ? 1 : 2;   // bytes per K/V element
-    if (rp.rows > 0) {
-      if (!a.q || !a.k_cache || !a.v_cache || !a.out)
-        return set_err(POD_ERR_INVALID, std::string(names[r]) + ": q, k_cache, v_cache and out are required");
-      if (a.q_stride_tok <= 0 || a.q_stride_head <= 0 || a.kv_stride_page <= 0 ||
-          a.kv_stride_tok <= 0 || a.kv_stride_head <= 0 || a.out_stride_tok <= 0 ||
-          a.out_stride_head <= 0)
-        return set_err(POD_ERR_INVALID, std::string(names[r]) + ": strides must be positive");
-      const uintptr_t mis = reinterpret_cast<uintptr_t>(a.q) | reinterpret_cast<uintptr_t>(a.k_cache) |
-                            reinterpret_cast<uintptr_t>(a.v_cache) | reinterpret_cast<uintptr_t>(a.out);
-      const int64_t smis = a.q_stride_tok | a.q_stride_head | a.kv_stride_page | a.kv_stride_tok |
-                           a.kv_stride_head | a.out_stride_tok | a.out_stride_head;
-      if ((mis & 15) || (smis & 7))
-        return set_err(POD_ERR_INVALID, std::string(names[r]) +
-                                             ": buffers must be 16-byte aligned and strides multiples of 8 elements");
-      if (fp8 && ((a.kv_stride_page | a.kv_stride_tok | a.kv_stride_head) & 15))
-        return set_err(POD_ERR_INVALID, "decode: FP8 K/V strides must be multiples of 16 elements");
-      if (fp8 && !a.kv_indices)
-        return set_err(POD_ERR_INVALID, "decode: FP8 K/V needs kv_indices (no identity page table)");
-      const int64_t lim = (int64_t)1 << 30;   // bytes = 2 * elements must stay below 2^31
-      if (a.kv_stride_page >= lim || a.kv_stride_tok >= lim || a.kv_stride_head >= lim)
-        return set_err(POD_ERR_UNSUPPORTED, std::string(names[r]) +
-                                                ": KV pool strides must be below 2^30 elements");
-      if (a.lse && (reinterpret_cast<uintptr_t>(a.lse) & 3))
-        return set_err(POD_ERR_INVALID, std::string(names[r]) + ": lse must be 4-byte aligned");
-    }
-    o.q = a.q;
-    o.q_st = a.q_stride_tok;
-    o.q_sh = a.q_stride_head;
-    o.k = a.k_cache;
-    o.v = a.v_cache;
-    o.kv_sp_b = (uint32_t)(a.kv_stride_page * esz);
-    o.kv_st_b = (uint32_t)(a.kv_stride_tok * esz);
-    o.kv_sh_b = (uint32_t)(a.kv_stride_head * esz);
-    o.kv_fp8 = fp8 ? 1 : 0;
-    o.indices = a.kv_indices;
-    o.out = a.out;
-    o.o_st = a.out_stride_tok;
-    o.o_sh = a.out_stride_head;
-    o.lse = a.lse;
-    // the decode role's FP8 calibration: q_scale * k_scale fold into the scale,
-    // v_scale into the output normalisation (0 = 1)
-    const float qk = r == 1 ? qk_d : 1.f;
-    o.scale_log2 = rp.sm_scale * qk * 1.4426950408889634f;
-    o.v_scale = r == 1 ? one(args->v_scale_d) : 1.f;
-    o.causal = rp.causal;
-    o.window_left = rp.window_left;
-  }
+  const int rc = fill_params(ctx->shape, args, p);
+  if (rc) return rc;
   p.image = ctx->graph ? reinterpret_cast<int32_t*>(ctx->int_ws) : int_half(ctx, ctx->cur);
   p.partials = reinterpret_cast<float*>(ctx->float_ws);
-  p.sinks = args->sinks;
-  p.num_qo_heads = ctx->num_qo_heads;
-  p.num_kv_heads = ctx->num_kv_heads;
-  p.group_size = ctx->num_qo_heads / ctx->num_kv_heads;
-  p.page_size = ctx->page_size;
-  p.page_shift = -1;
-  for (int sh = 0; sh < 31; ++sh)
-    if ((1 << sh) == ctx->page_size) p.page_shift = sh;
   DeviceGuard dg(ctx->device);
   if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (ctx->graph) {
     // the image copy went on the plan's stream, ahead of this launch; no event
     // work, so the call can be captured into a graph
-    const int e = pod::launch_pod_grid(p, ctx->dtype, ctx->info.grid, stream, nullptr);
+    const int e = pod::launch_pod_grid(p, ctx->shape.dtype, ctx->info.grid, stream, nullptr);
     if (e != (int)hipSuccess) return hip_err((hipError_t)e, "pod grid launch");
     g_err.clear();
     return POD_OK;
@@ -462,7 +497,7 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
   }
   // used[cur] fires when this launch completes (a launch that is not issued
   // because the plan holds no work reads nothing)
-  int e = pod::launch_pod_grid(p, ctx->dtype, ctx->info.grid, stream, ctx->used[ctx->cur]);
+  int e = pod::launch_pod_grid(p, ctx->shape.dtype, ctx->info.grid, stream, ctx->used[ctx->cur]);
   if (e != (int)hipSuccess) return hip_err((hipError_t)e, "pod grid launch");
   if (ctx->info.grid > 0) ctx->used_pending[ctx->cur] = true;
   g_err.clear();
@@ -492,6 +527,61 @@ int pod_merge_states(const void* o_a, const float* lse_a, const void* o_b, const
   const int e = pod::launch_merge_states(o_a, lse_a, o_b, lse_b, o_out, lse_out, rows * num_heads,
                                          num_heads, dtype, sinks, stream);
   if (e != (int)hipSuccess) return hip_err((hipError_t)e, "merge launch");
+  g_err.clear();
+  return POD_OK;
+}
+
+int pod_run_static(const pod_plan_desc* desc, const pod_run_args* args, int device, void* stream) {
+  if (!desc) return set_err(POD_ERR_INVALID, "desc is NULL");
+  if (!args) return set_err(POD_ERR_INVALID, "args is NULL");
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_err(e, "hipGetDeviceCount");
+  if (device < 0 || device >= ndev || device >= pod::kMaxDevices)
+    return set_err(POD_ERR_INVALID, "device index out of range");
+  DeviceGuard dg(device);
+  if (!dg.ok) return set_err(POD_ERR_HIP, "hipSetDevice failed");
+  pod_plan_desc d = *desc;
+  if (d.num_cus <= 0) {
+    e = hipDeviceGetAttribute(&d.num_cus, hipDeviceAttributeMultiprocessorCount, device);
+    if (e != hipSuccess) return hip_err(e, "hipDeviceGetAttribute");
+  }
+  void* base = nullptr;
+  const int se = pod::static_scratch(device, &base);
+  if (se != (int)hipSuccess) return hip_err((hipError_t)se, "hipGetSymbolAddress (static scratch)");
+
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  size_t words = 0;
+  bool fits = false;
+  pod_plan_info inf;
+  std::string err;
+  int rc = pod::plan_compute(d, [&](size_t n) -> int32_t* {
+    words = n;
+    fits = n * sizeof(int32_t) <= pod::kStaticImageBytes;
+    return fits ? g_static_image : nullptr;
+  }, inf, &err);
+  if (rc) return set_err(rc, err);
+  if (!fits)
+    return set_err(POD_ERR_WORKSPACE, "work list of " + std::to_string(words * 4) +
+                                          " bytes exceeds the static limit of 16 MiB");
+  if ((size_t)inf.float_ws_bytes > pod::kStaticPartialBytes)
+    return set_err(POD_ERR_WORKSPACE, "split-KV partial states of " + std::to_string(inf.float_ws_bytes) +
+                                          " bytes exceed the static limit of 48 MiB");
+  PlanShape shape;
+  plan_shape(d, shape);
+  pod::Params p{};
+  rc = fill_params(shape, args, p);
+  if (rc) return rc;
+  p.image = reinterpret_cast<int32_t*>(base);
+  p.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(base) + pod::kStaticImageBytes);
+  // the image (its arrival counters and pool queue zero) goes up on the
+  // caller's stream ahead of the launch; the host buffer is free again when
+  // the copy call returns (host memory that is not pinned is staged at once)
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  e = hipMemcpyAsync(base, g_static_image, words * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (work list)");
+  const int le = pod::launch_pod_grid(p, d.dtype, inf.grid, stream, nullptr);
+  if (le != (int)hipSuccess) return hip_err((hipError_t)le, "pod grid launch");
   g_err.clear();
   return POD_OK;
 }

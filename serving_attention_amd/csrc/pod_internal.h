@@ -32,6 +32,12 @@ constexpr int kTdescWords = 8;
 constexpr int kMaxSinkHeads = 1024;    // sinks staged in LDS by the query tiles
 constexpr int kMaxKvHeads = 16384;     // kv head index fits the block-table entry
 constexpr int kMaxTilesPerWg = 65536;  // tile index fits the block-table entry
+// Static scratch of the allocation-free entry point (one copy per device): the
+// work-list image, then split-KV partial states.
+constexpr size_t kStaticImageBytes = (size_t)16 << 20;
+constexpr size_t kStaticPartialBytes = (size_t)48 << 20;
+constexpr size_t kStaticScratchBytes = kStaticImageBytes + kStaticPartialBytes;
+constexpr int kMaxDevices = 64;
 
 // Block-table entry of a workgroup's query-tile stream:
 //   {first key of the block, last key of its item, first page of the request, meta}
@@ -98,6 +104,10 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
 // Launch the fused grid on `stream` (a hipStream_t); `done_event` (a hipEvent_t,
 // or null) is signalled when the launch completes. Returns a hipError_t value.
 int launch_pod_grid(const Params& p, int dtype, int grid, void* stream, void* done_event);
+// Device address of the calling thread's current device's static scratch array
+// (kStaticScratchBytes, 256-byte aligned), looked up once per device. `device`
+// must be the current device. Returns a hipError_t value.
+int static_scratch(int device, void** ptr);
 // Cascade merge of n_pairs (row, head) states of head_dim 128 (merge_kernels.hip).
 int launch_merge_states(const void* oa, const float* la, const void* ob, const float* lb,
                         void* oo, float* lo, int64_t n_pairs, int heads, int dtype,

@@ -36,9 +36,17 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "pod_internal.h"
+
+// Scratch memory of pod_run_static, for callers that cannot allocate: the
+// work-list image followed by split-KV partial states. Every device the
+// library runs on holds one copy until the process ends. Host code never uses
+// this name as an address: it takes each device's copy from
+// pod::static_scratch, which looks it up with hipGetSymbolAddress.
+static __device__ __align__(256) char scratch[pod::kStaticScratchBytes];
 
 namespace pod {
 namespace {
@@ -1561,6 +1569,23 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
 }
 
 }  // namespace
+
+int static_scratch(int device, void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    // with `device` current: this device's copy of the array
+    void* a = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!a) return (int)hipErrorInvalidSymbol;
+    addr[device] = a;
+  }
+  *ptr = addr[device];
+  return (int)hipSuccess;
+}
 
 int launch_pod_grid(const Params& p, int dtype, int grid, void* stream, void* done_event) {
   if (grid <= 0) return (int)hipSuccess;

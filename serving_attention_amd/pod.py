@@ -74,6 +74,109 @@ def kv_views(cache: KVCache, kv_layout: str):
     raise ValueError(f"unknown kv_layout {kv_layout!r}")
 
 
+def _plan_record(keep, present, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sinks,
+                 kv_dtype_d) -> dict:
+    """What run() checks its tensors against. keep holds (qo, kv, lpl) of each
+    present role, prefill first."""
+    nnz, rows = [], []
+    k = 0
+    for here in present:
+        if not here:
+            rows.append(0)
+            nnz.append(0)
+        else:
+            rows.append(int(keep[k][-1]))
+            nnz.append(int(keep[k + 1][-1]))
+            k += 3
+    return dict(rows=tuple(rows), nnz=tuple(nnz), num_qo_heads=int(num_qo_heads),
+                num_kv_heads=int(num_kv_heads), head_dim=int(head_dim), page_size=int(page_size),
+                dtype=_dtype_code(dtype), sinks=bool(sinks), fp8_d=kv_dtype_d == torch.float8_e4m3fn)
+
+
+def _role_args(pl, kv_layout, graph, idx, q, cache, kv_indices, out, lse):
+    """One role's pod_role_args, checked against the plan record."""
+    rows = pl["rows"][idx]
+    if rows == 0 or q is None:
+        return _lib.PodRoleArgs()
+    hq, d = pl["num_qo_heads"], pl["head_dim"]
+    # graph mode: buffers sized for the largest plan
+    short = q.shape[0] < rows if graph else q.shape[0] != rows
+    if q.dim() != 3 or short or q.shape[1] != hq or q.shape[2] != d:
+        raise ValueError(f"q must be [{rows}, {hq}, {d}], got {tuple(q.shape)}")
+    if _DT.get(q.dtype) != pl["dtype"]:
+        raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "q dtype differs from the planned dtype")
+    if q.stride(-1) != 1:
+        raise ValueError("q: head_dim must be dense")
+    k, v, sp, st, sh = kv_views(cache, kv_layout)
+    want = torch.float8_e4m3fn if (idx == 1 and pl["fp8_d"]) else q.dtype
+    if k.dtype != want:
+        raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, f"kv dtype {k.dtype} differs from the planned {want}")
+    ps = k.shape[1] if kv_layout == "NHD" else k.shape[2]
+    hk = k.shape[2] if kv_layout == "NHD" else k.shape[1]
+    if ps != pl["page_size"] or hk != pl["num_kv_heads"] or k.shape[3] != d:
+        raise ValueError("paged cache shape differs from the plan")
+    nnz = pl["nnz"][idx]
+    if kv_indices is not None:
+        if kv_indices.dtype != torch.int32 or not kv_indices.is_cuda or kv_indices.dim() != 1:
+            raise ValueError("kv_indices must be a 1-D int32 device tensor")
+        if kv_indices.numel() < nnz:
+            raise ValueError(f"kv_indices holds {kv_indices.numel()} pages, the plan needs {nnz}")
+    elif k.shape[0] < nnz:
+        raise ValueError(f"identity page table needs {nnz} pages, the cache has {k.shape[0]}")
+    # outputs: the kernel writes 16-byte vectors of a dense head_dim and the
+    # LSE at row * num_qo_heads + head
+    if not isinstance(out, torch.Tensor) or out.dim() != 3 or out.shape[0] < q.shape[0] \
+            or out.shape[1] != hq or out.shape[2] != d:
+        raise ValueError(f"out must be [{q.shape[0]}, {hq}, {d}]")
+    if out.dtype != q.dtype or out.device != q.device or out.stride(-1) != 1:
+        raise ValueError("out must have q's dtype and device and a dense head_dim")
+    if lse is not None:
+        if lse.dim() != 2 or lse.shape[0] < q.shape[0] or lse.shape[1] != hq:
+            raise ValueError(f"lse must be [{q.shape[0]}, {hq}]")
+        if lse.dtype != torch.float32 or lse.device != q.device or lse.stride() != (hq, 1):
+            raise ValueError("lse must be a contiguous float32 tensor on q's device")
+    return _lib.PodRoleArgs(
+        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), v.data_ptr(), sp, st, sh,
+        kv_indices.data_ptr() if kv_indices is not None else None,
+        out.data_ptr(), out.stride(0), out.stride(1),
+        lse.data_ptr() if lse is not None else None)
+
+
+def _run_args(pl, kv_layout, graph, q_p, paged_kv_cache_p, kv_indices_p, q_d, paged_kv_cache_d,
+              kv_indices_d, sinks, return_lse, out_p, out_d, lse_p, lse_d, q_scale_d, k_scale_d,
+              v_scale_d):
+    """pod_run_args for one launch, with the outputs it writes (allocated here
+    when not given)."""
+    hq, d = pl["num_qo_heads"], pl["head_dim"]
+    outs, lses = [], []
+    for idx, q, o, l in ((0, q_p, out_p, lse_p), (1, q_d, out_d, lse_d)):
+        rows = pl["rows"][idx]
+        if q is None:
+            if rows:
+                raise ValueError("a planned role needs its q tensor")
+            outs.append(None)
+            lses.append(None)
+            continue
+        n = q.shape[0] if graph else rows
+        if o is None:
+            o = torch.empty((n, hq, d), dtype=q.dtype, device=q.device)
+        if l is None and return_lse:
+            l = torch.empty((n, hq), dtype=torch.float32, device=q.device)
+        outs.append(o)
+        lses.append(l)
+    if pl["sinks"]:
+        if sinks is None or sinks.dtype != torch.float32 or sinks.numel() != hq or not sinks.is_cuda:
+            raise ValueError("plan has sinks: pass an fp32 [num_qo_heads] device tensor")
+    elif sinks is not None:
+        raise ValueError("plan has no sinks")
+    args = _lib.PodRunArgs(
+        _role_args(pl, kv_layout, graph, 0, q_p, paged_kv_cache_p, kv_indices_p, outs[0], lses[0]),
+        _role_args(pl, kv_layout, graph, 1, q_d, paged_kv_cache_d, kv_indices_d, outs[1], lses[1]),
+        sinks.data_ptr() if sinks is not None else None,
+        float(q_scale_d or 0.0), float(k_scale_d or 0.0), float(v_scale_d or 0.0))
+    return args, outs, lses
+
+
 class BatchPOD:
     """Batch prefill + batch decode paged attention in one launch per run()."""
 
@@ -186,77 +289,15 @@ class BatchPOD:
             kv_dtype_d=kv_dtype_d)
         s = _stream_handle(self.device) if stream is None else ctypes.c_void_p(stream)
         _lib.check(self._lib.pod_plan(self._ctx, ctypes.byref(desc), s))
-        # keep holds (qo, kv, lpl) of each role that is present, prefill first
-        nnz = []
-        rows = []
-        k = 0
-        for qo in (qo_indptr_p, qo_indptr_d):
-            if qo is None:
-                rows.append(0)
-                nnz.append(0)
-            else:
-                rows.append(int(keep[k][-1]))
-                nnz.append(int(keep[k + 1][-1]))
-                k += 3
-        self._planned = dict(
-            rows=tuple(rows), nnz=tuple(nnz),
-            num_qo_heads=int(num_qo_heads), num_kv_heads=int(num_kv_heads),
-            head_dim=int(head_dim), page_size=int(page_size), dtype=_dtype_code(dtype),
-            sinks=bool(sinks), fp8_d=kv_dtype_d == torch.float8_e4m3fn)
+        self._planned = _plan_record(keep, (qo_indptr_p is not None, qo_indptr_d is not None),
+                                     num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sinks,
+                                     kv_dtype_d)
         return self
 
     def plan_info(self) -> dict:
         info = _lib.PodPlanInfo()
         _lib.check(self._lib.pod_plan_stats(self._ctx, ctypes.byref(info)))
         return info.as_dict()
-
-    def _role_args(self, idx, q, cache, kv_indices, out, lse):
-        pl = self._planned
-        rows = pl["rows"][idx]
-        if rows == 0 or q is None:
-            return _lib.PodRoleArgs()
-        hq, d = pl["num_qo_heads"], pl["head_dim"]
-        # graph mode: buffers sized for the largest plan
-        short = q.shape[0] < rows if self.use_cuda_graph else q.shape[0] != rows
-        if q.dim() != 3 or short or q.shape[1] != hq or q.shape[2] != d:
-            raise ValueError(f"q must be [{rows}, {hq}, {d}], got {tuple(q.shape)}")
-        if _DT.get(q.dtype) != pl["dtype"]:
-            raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "q dtype differs from the planned dtype")
-        if q.stride(-1) != 1:
-            raise ValueError("q: head_dim must be dense")
-        k, v, sp, st, sh = kv_views(cache, self.kv_layout)
-        want = torch.float8_e4m3fn if (idx == 1 and pl["fp8_d"]) else q.dtype
-        if k.dtype != want:
-            raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, f"kv dtype {k.dtype} differs from the planned {want}")
-        ps = k.shape[1] if self.kv_layout == "NHD" else k.shape[2]
-        hk = k.shape[2] if self.kv_layout == "NHD" else k.shape[1]
-        if ps != pl["page_size"] or hk != pl["num_kv_heads"] or k.shape[3] != d:
-            raise ValueError("paged cache shape differs from the plan")
-        nnz = pl["nnz"][idx]
-        if kv_indices is not None:
-            if kv_indices.dtype != torch.int32 or not kv_indices.is_cuda or kv_indices.dim() != 1:
-                raise ValueError("kv_indices must be a 1-D int32 device tensor")
-            if kv_indices.numel() < nnz:
-                raise ValueError(f"kv_indices holds {kv_indices.numel()} pages, the plan needs {nnz}")
-        elif k.shape[0] < nnz:
-            raise ValueError(f"identity page table needs {nnz} pages, the cache has {k.shape[0]}")
-        # outputs: the kernel writes 16-byte vectors of a dense head_dim and the
-        # LSE at row * num_qo_heads + head
-        if not isinstance(out, torch.Tensor) or out.dim() != 3 or out.shape[0] < q.shape[0] \
-                or out.shape[1] != hq or out.shape[2] != d:
-            raise ValueError(f"out must be [{q.shape[0]}, {hq}, {d}]")
-        if out.dtype != q.dtype or out.device != q.device or out.stride(-1) != 1:
-            raise ValueError("out must have q's dtype and device and a dense head_dim")
-        if lse is not None:
-            if lse.dim() != 2 or lse.shape[0] < q.shape[0] or lse.shape[1] != hq:
-                raise ValueError(f"lse must be [{q.shape[0]}, {hq}]")
-            if lse.dtype != torch.float32 or lse.device != q.device or lse.stride() != (hq, 1):
-                raise ValueError("lse must be a contiguous float32 tensor on q's device")
-        return _lib.PodRoleArgs(
-            q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), v.data_ptr(), sp, st, sh,
-            kv_indices.data_ptr() if kv_indices is not None else None,
-            out.data_ptr(), out.stride(0), out.stride(1),
-            lse.data_ptr() if lse is not None else None)
 
     def run(self, q_p, paged_kv_cache_p, kv_indices_p, q_d, paged_kv_cache_d, kv_indices_d, *,
             sinks: Optional[torch.Tensor] = None, return_lse: bool = False,
@@ -271,34 +312,10 @@ class BatchPOD:
         """
         if self._planned is None:
             raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "run() before plan()")
-        pl = self._planned
-        hq, d = pl["num_qo_heads"], pl["head_dim"]
-        outs, lses = [], []
-        for idx, q, o, l in ((0, q_p, out_p, lse_p), (1, q_d, out_d, lse_d)):
-            rows = pl["rows"][idx]
-            if q is None:
-                if rows:
-                    raise ValueError("a planned role needs its q tensor")
-                outs.append(None)
-                lses.append(None)
-                continue
-            n = q.shape[0] if self.use_cuda_graph else rows
-            if o is None:
-                o = torch.empty((n, hq, d), dtype=q.dtype, device=q.device)
-            if l is None and return_lse:
-                l = torch.empty((n, hq), dtype=torch.float32, device=q.device)
-            outs.append(o)
-            lses.append(l)
-        if pl["sinks"]:
-            if sinks is None or sinks.dtype != torch.float32 or sinks.numel() != hq or not sinks.is_cuda:
-                raise ValueError("plan has sinks: pass an fp32 [num_qo_heads] device tensor")
-        elif sinks is not None:
-            raise ValueError("plan has no sinks")
-        args = _lib.PodRunArgs(
-            self._role_args(0, q_p, paged_kv_cache_p, kv_indices_p, outs[0], lses[0]),
-            self._role_args(1, q_d, paged_kv_cache_d, kv_indices_d, outs[1], lses[1]),
-            sinks.data_ptr() if sinks is not None else None,
-            float(q_scale_d or 0.0), float(k_scale_d or 0.0), float(v_scale_d or 0.0))
+        args, outs, lses = _run_args(self._planned, self.kv_layout, self.use_cuda_graph, q_p,
+                                     paged_kv_cache_p, kv_indices_p, q_d, paged_kv_cache_d, kv_indices_d,
+                                     sinks, return_lse, out_p, out_d, lse_p, lse_d,
+                                     q_scale_d, k_scale_d, v_scale_d)
         _lib.check(self._lib.pod_run(self._ctx, ctypes.byref(args), _stream_handle(self.device)))
         if return_lse:
             return (outs[0], lses[0]), (outs[1], lses[1])
@@ -389,3 +406,44 @@ def merge_states(o_a: torch.Tensor, lse_a: torch.Tensor, o_b: torch.Tensor, lse_
                                     o_a.device.index if o_a.device.index is not None else 0,
                                     _stream_handle(o_a.device)))
     return out, lse_out
+
+
+def run_static(qo_indptr_p, kv_indptr_p, last_page_len_p, qo_indptr_d, kv_indptr_d, last_page_len_d,
+               q_p, paged_kv_cache_p, kv_indices_p, q_d, paged_kv_cache_d, kv_indices_d, *,
+               num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int,
+               dtype=torch.bfloat16, kv_layout: str = "NHD", causal_p: bool = True, causal_d: bool = True,
+               window_left_p: int = -1, window_left_d: int = -1, sm_scale_p: Optional[float] = None,
+               sm_scale_d: Optional[float] = None, decode_chunk: int = 0, order: int = 0,
+               kv_dtype_d=None, sinks: Optional[torch.Tensor] = None, return_lse: bool = False,
+               out_p=None, out_d=None, lse_p=None, lse_d=None, q_scale_d: Optional[float] = None,
+               k_scale_d: Optional[float] = None, v_scale_d: Optional[float] = None):
+    """BatchPOD(...).plan(...) and .run(...) in one call of pod_run_static: no
+    context and no workspace; the work list and split-KV partial states use the
+    library's static device scratch (for callers that cannot allocate device
+    memory; pass out/lse tensors to allocate nothing here either). Same
+    arguments and results as plan() and run(); the plan's `sinks` flag follows
+    from whether a sinks tensor is passed."""
+    if kv_layout not in ("NHD", "HND"):
+        raise ValueError(f"unknown kv_layout {kv_layout!r}")
+    has_sinks = sinks is not None
+    desc, keep = BatchPOD._plan_desc(
+        qo_indptr_p, kv_indptr_p, last_page_len_p, qo_indptr_d, kv_indptr_d, last_page_len_d,
+        num_qo_heads=num_qo_heads, num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size,
+        dtype=dtype, causal_p=causal_p, causal_d=causal_d, window_left_p=window_left_p,
+        window_left_d=window_left_d, sm_scale_p=sm_scale_p, sm_scale_d=sm_scale_d, sinks=has_sinks,
+        decode_chunk=decode_chunk, order=order, kv_dtype_d=kv_dtype_d)
+    pl = _plan_record(keep, (qo_indptr_p is not None, qo_indptr_d is not None), num_qo_heads,
+                      num_kv_heads, head_dim, page_size, dtype, has_sinks, kv_dtype_d)
+    args, outs, lses = _run_args(pl, kv_layout, False, q_p, paged_kv_cache_p, kv_indices_p, q_d,
+                                 paged_kv_cache_d, kv_indices_d, sinks, return_lse, out_p, out_d, lse_p,
+                                 lse_d, q_scale_d, k_scale_d, v_scale_d)
+    ref = q_p if q_p is not None else q_d
+    if ref is None or not ref.is_cuda:
+        raise ValueError("run_static needs device query tensors")
+    dev = ref.device.index if ref.device.index is not None else torch.cuda.current_device()
+    lib = _lib.load()
+    _lib.check(lib.pod_run_static(ctypes.byref(desc), ctypes.byref(args), dev, _stream_handle(ref.device)))
+    del keep
+    if return_lse:
+        return (outs[0], lses[0]), (outs[1], lses[1])
+    return outs[0], outs[1]
