@@ -116,6 +116,9 @@ constexpr int kLdsMain = kMax2(kMax2(kRingSlots * kTileBuf, kWaves * kWaveLds), 
 static_assert(kLdsMain + kRingSlots * kIdSlot <= 160 * 1024, "LDS budget");
 // the running max moves only when a block's max exceeds it by this much (log2 units)
 constexpr float kRescaleThreshold = 8.f;
+// Query tiles: largest sum of one block's exponentials (one lane, 32 keys) taken
+// without moving the row's reference maximum.
+constexpr float kBlockSumLimit = 0x1p64f;
 // Start of a query-tile row's running max (raw score units): finite, so the
 // bound test and the exponent need no case for a row that has seen no valid
 // key yet. The max is only a reference point (P = exp2(sl2 (s - m)) for any m
@@ -178,6 +181,15 @@ __device__ __forceinline__ uint32_t lds_addr(const char* p) {
 __device__ __forceinline__ void lds_dma16(const void* src, const char* dst) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :: "v"(src), "s"(lds_addr(dst)) : "memory", "m0");
+}
+// the same with the LDS destination given as a wave-uniform LDS byte address
+__device__ __forceinline__ void lds_dma16_at(const void* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(dst) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4_at(const void* src, uint32_t dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(dst) : "memory", "m0");
 }
 __device__ __forceinline__ void lds_dma4(const void* src, const char* dst) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -486,10 +498,12 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
   // table and the identity page is used instead.
   auto idslot = [&](int v) { return idring + (v & (kRingSlots - 1)) * kIdSlot + wave * 256; };
   auto slot = [&](int v) { return ring + (v & (kRingSlots - 1)) * kTileBuf; };
+  // the same slots as LDS byte addresses (wave-uniform), for the direct loads
+  const uint32_t ring_at = lds_addr(ring), idring_at = lds_addr(idring) + wave * 256;
   auto load_ids = [&](int v, const Ent& e) {
     const int kb = e.kb, kl = e.kl, ps = e.ps;
     const uint32_t pl = (uint32_t)pm.page(min(kb + lane, kl));
-    lds_dma4(id_src + (paged ? ps + pl : 0u), idslot(v));
+    lds_dma4_at(id_src + (paged ? ps + pl : 0u), idring_at + (v & (kRingSlots - 1)) * kIdSlot);
   };
   int32_t pid[2];
   auto read_ids = [&](int v) {
@@ -499,14 +513,14 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
   // the K and V loads of the wave's row group u of block v
   auto dma_rows = [&](int v, int u, const Ent& e) {
     const int kb = e.kb, kl = e.kl, ps = e.ps;
-    const uint32_t kvh = (e.meta >> kEntKvhShift) & 0x3fff;
+    // the block's kv head: a wave-uniform offset of both pools
+    const uint64_t hoff = (uint64_t)((e.meta >> kEntKvhShift) & 0x3fff) * kv_sh;
     const int key = min(kb + rr[u], kl);
     const uint32_t page = paged ? (uint32_t)pid[u] : (uint32_t)(ps + pm.page(key));
-    const uint64_t ro = (uint64_t)page * kv_sp + (uint32_t)pm.slot(key) * kv_st +
-                        (uint64_t)kvh * kv_sh + (lslot << 4);
-    char* dst = slot(v);
-    lds_dma16(kpool + ro, dst + (2 * wave + u) * kTileKGroup);
-    lds_dma16(vpool + ro, dst + kTileKBytes + (2 * wave + u) * kTileVGroup);
+    const uint64_t ro = (uint64_t)page * kv_sp + ((uint32_t)pm.slot(key) * kv_st + (lslot << 4));
+    const uint32_t dst = ring_at + (v & (kRingSlots - 1)) * kTileBuf;
+    lds_dma16_at(kpool + hoff + ro, dst + (2 * wave + u) * kTileKGroup);
+    lds_dma16_at(vpool + hoff + ro, dst + kTileKBytes + (2 * wave + u) * kTileVGroup);
   };
   auto dma_block = [&](int v, const Ent& e) {
     dma_rows(v, 0, e);
@@ -650,7 +664,8 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
   // Each block b is two phases of a wave:
   //   M: the score MFMAs of block b (S_b, 16, K from LDS slot b) and the P.V
   //      MFMAs of block b-1 (16, V^T from slot b-1, P_{b-1} in registers);
-  //   V: mask, running max and exponentials of S_b (P_b and l), VALU only.
+  //   V: mask and exponentials of S_b (P_b and l), VALU only; the running
+  //      max moves only when a block's sum shows it must.
   // Waves 0-3 run M while waves 4-7 (the other wave of each SIMD) run V, then
   // the other way round, with a barrier between the turns: the MFMA pipe takes
   // one wave's 32 MFMAs while the VALU runs the other wave's softmax.
@@ -702,7 +717,6 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
     }
   };
   auto v_phase = [&](int kb) {
-    __builtin_amdgcn_s_setprio(1);
     if (__any((unsigned)(kb - rm.lo) > rm.span || (unsigned)(kb + kTileKeys - 1 - rm.lo) > rm.span)) {
       // key of accumulator j = kb + 8 hi + (its constant part); the lane part
       // is opaque so that the 32 key offsets are not held in registers
@@ -717,49 +731,58 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
           s[h][j] = ((unsigned)kidx <= rm.span) ? s[h][j] : kNegInf;
         }
     }
-    // block max: two chains of three-way maxima, then the other lane half
-    float mx0 = max3_raw(s[0][0], s[0][1], s[0][2]);
-    float mx1 = max3_raw(s[1][0], s[1][1], s[1][2]);
+    // Exponentials against the row's current reference m (raw units, the
+    // same in both lane halves of a row), then one test of the block's sum:
+    // it passes 2^64 only if a score sits far above m (always in a row's
+    // first block with a valid key, whose m is still kMaxInit; rarely after),
+    // and only then is the block maximum taken, the state rescaled and the
+    // exponentials redone. Below that bound P, l and O stay finite in fp32
+    // and bf16, and their ratio does not depend on m.
+    float la[4];
+    auto exps = [&](float mu2) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 3; j < 15; j += 2) {
-      mx0 = max3_raw(mx0, s[0][j], s[0][j + 1]);
-      mx1 = max3_raw(mx1, s[1][j], s[1][j + 1]);
-    }
-    mx0 = max3_raw(mx0, s[0][15], s[1][15]);
-    {
-      const float mx = max_raw(mx0, mx1);
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx0 = max_raw(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    // the max moves only past the threshold (rare after a row's first valid
-    // key); lanes that keep theirs scale by exp2(0) = 1
-    const bool upd = (mx0 - m) * sl2 > kRescaleThreshold;
-    if (__any(upd)) {
-      const float mn = upd ? mx0 : m;
-      const float alpha = fast_exp2((m - mn) * sl2);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float e = fast_exp2(fmaf(s[h][8 * hh + i], sl2, -mu2));
+            la[i & 3] = (h == 0 && hh == 0 && i < 4) ? e : la[i & 3] + e;
+            pb[h][hh][i] = (T)e;
+          }
+    };
+    // (kMaxInit * sl2 is finite for every accepted scale; while no key is
+    // valid every score is -inf and every exponential 0)
+    exps(m * sl2);
+    float bsum = (la[0] + la[1]) + (la[2] + la[3]);
+    if (__any(!(bsum <= kBlockSumLimit))) {
+      // block max: two chains of three-way maxima, then the other lane half
+      float mx0 = max3_raw(s[0][0], s[0][1], s[0][2]);
+      float mx1 = max3_raw(s[1][0], s[1][1], s[1][2]);
+#pragma unroll
+      for (int j = 3; j < 15; j += 2) {
+        mx0 = max3_raw(mx0, s[0][j], s[0][j + 1]);
+        mx1 = max3_raw(mx1, s[1][j], s[1][j + 1]);
+      }
+      mx0 = max3_raw(mx0, s[0][15], s[1][15]);
+      {
+        const float mx = max3_raw(mx0, mx1, m);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx0 = max_raw(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // the reference only moves up; rows whose block stays below it keep it
+      // and scale by exp2(0) = 1
+      const float alpha = fast_exp2((m - mx0) * sl2);
       l *= alpha;
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int j = 0; j < 16; ++j) o[b][j] *= alpha;
-      m = mn;
+      m = mx0;
+      exps(m * sl2);
+      bsum = (la[0] + la[1]) + (la[2] + la[3]);
     }
-    // (kMaxInit * sl2 is finite for every accepted scale; while no key is
-    // valid every score is -inf and every exponential 0)
-    const float mu2 = m * sl2;
-    float la[4];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float e = fast_exp2(fmaf(s[h][8 * hh + i], sl2, -mu2));
-          la[i & 3] = (h == 0 && hh == 0 && i < 4) ? e : la[i & 3] + e;
-          pb[h][hh][i] = (T)e;
-        }
-    l += (la[0] + la[1]) + (la[2] + la[3]);
-    __builtin_amdgcn_s_setprio(0);
+    l += bsum;
   };
 
   // Block v streams into ring slot v % 4 and its page ids into id slot v % 4.
