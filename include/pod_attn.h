@@ -118,11 +118,13 @@ typedef struct pod_role_desc {
  *                 the FP8 KV cache whose calibration scales the POD article lists
  *                 with the decode run parameters ([POD] "Decode 侧参数与'plan 覆盖'行为"). q and O stay
  *                 `dtype`; values are widened exactly to `dtype` inside the launch.
- *                 Supported only where every decode (request, kv head) runs as one
- *                 key-chunk item, i.e. q_len * group <= 32 rows (POD_ERR_UNSUPPORTED
- *                 otherwise). The prefill role keeps `dtype` K/V. An FP8 decode role
- *                 needs kv_indices at pod_run (POD_ERR_INVALID for NULL) and K/V strides
- *                 that are multiples of 16 elements.
+ *                 Every decode (request, kv head) then runs as key chunks: requests
+ *                 with more than 32 rows (q_len * group) are cut into 32-row slices
+ *                 over the same keys (each slice reads the K/V rows again, from the
+ *                 die's L2 when its slices run together). The prefill role keeps
+ *                 `dtype` K/V. An FP8 decode role needs kv_indices at pod_run
+ *                 (POD_ERR_INVALID for NULL) and K/V strides that are multiples of
+ *                 16 elements.
  */
 typedef struct pod_plan_desc {
   pod_role_desc prefill;
@@ -390,8 +392,10 @@ int pod_run_static(const pod_plan_desc* desc, const pod_run_args* args, int devi
  *     requests first, then decode requests.
  *   items[n_items][8]: {flags, req, kv_head, tok0, ntok, kv_begin, kv_end, group}.
  *     flags bit 0: role (0 prefill, 1 decode); bit 1: kind (0 = query tile of up
- *     to 256 rows, 1 = key chunk of all q_len*group rows, <= 32); bits 8..: split
- *     index. group == -1: the item writes its output directly. Items are grouped
+ *     to 256 rows, tokens tok0 .. tok0 + ntok - 1; 1 = key chunk of up to 32 of the
+ *     request's q_len*group rows, from row tok0 on (a multiple of 32; ntok =
+ *     q_len)); bits 8..: split index. group == -1: the item writes its output
+ *     directly. Items are grouped
  *     by workgroup (its query tiles, then its key chunks); the last pool_count
  *     items, from pool_first on, are key chunks that any workgroup takes from a
  *     shared queue once its own list is done.
@@ -404,7 +408,8 @@ int pod_run_static(const pod_plan_desc* desc, const pod_run_args* args, int devi
  *     {first key, last key of the item, first page of the request, meta}; meta
  *     bit 31 first block of its item, bit 30 role, bits 16..29 kv head, bits
  *     0..15 tile index in the workgroup's list.
- *   groups[n_groups][4]: {n_splits, first_slot, req, kv_head}.
+ *   groups[n_groups][4]: {n_splits, first_slot, req, kv_head}, one per (request,
+ *     kv head, row slice) whose keys are split.
  *   counters[n_groups]: arrival counters, zero in the image.
  *   queue[2]: next pool item and workgroups done with the pool, zero in the image.
  */

@@ -161,20 +161,24 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
     int64_t p0 = (int64_t)q.kv_len - q.qo_len;
     return r.window_left >= 0 ? std::max<int64_t>(0, p0 - r.window_left) : 0;
   };
-  auto is_chunk = [&](const Req& q) { return (int64_t)q.qo_len * g <= kChunkRows; };
-
   if (d.decode_kv_dtype != 0 && d.decode_kv_dtype != d.dtype && d.decode_kv_dtype != POD_DTYPE_FP8_E4M3)
     return fail(err, POD_ERR_UNSUPPORTED, "decode_kv_dtype must be 0, dtype or POD_DTYPE_FP8_E4M3");
-  if (d.decode_kv_dtype == POD_DTYPE_FP8_E4M3)
-    for (const Req& q : reqs)
-      if (q.role == 1 && q.qo_len > 0 && !is_chunk(q))
-        return fail(err, POD_ERR_UNSUPPORTED,
-                    "FP8 decode K/V needs q_len * group <= 32 rows per request (key-chunk items)");
+  const bool fp8_d = d.decode_kv_dtype == POD_DTYPE_FP8_E4M3;
+  // Key chunks hold up to 32 rows (q_len x group) of one (request, kv head).
+  // Requests with more rows run as query tiles, except on an FP8 decode cache
+  // (its bytes are widened as a key chunk stages them): those are cut into row
+  // slices of 32, each a key chunk of its own over the same keys.
+  auto is_chunk = [&](const Req& q) {
+    return (int64_t)q.qo_len * g <= kChunkRows || (q.role == 1 && fp8_d);
+  };
+  auto n_slices = [&](const Req& q) -> int64_t {
+    return ((int64_t)q.qo_len * g + kChunkRows - 1) / kChunkRows;
+  };
 
   // decode split size: enough key-chunk items for ~4 per CU, at least 256 keys each
   int64_t chunk_keys_total = 0;
   for (const Req& q : reqs)
-    if (q.qo_len > 0 && is_chunk(q)) chunk_keys_total += (int64_t)H * (q.kv_len - chunk_lo(q));
+    if (q.qo_len > 0 && is_chunk(q)) chunk_keys_total += (int64_t)H * n_slices(q) * (q.kv_len - chunk_lo(q));
   int64_t C;
   if (d.decode_chunk < 0) {
     C = INT32_MAX;
@@ -190,7 +194,7 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
   size_t n_items_total = 0;
   for (const Req& q : reqs) {
     if (q.qo_len == 0) continue;
-    if (is_chunk(q)) n_items_total += (size_t)H * (size_t)((q.kv_len - chunk_lo(q) + C - 1) / C);
+    if (is_chunk(q)) n_items_total += (size_t)H * (size_t)n_slices(q) * (size_t)((q.kv_len - chunk_lo(q) + C - 1) / C);
     else n_items_total += (size_t)H * (size_t)((q.qo_len + T - 1) / T);
   }
   std::vector<Item> items(n_items_total);
@@ -204,30 +208,34 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
     if (is_chunk(q)) {
       const int64_t lo = chunk_lo(q), hi = q.kv_len;
       const int64_t splits = (hi - lo + C - 1) / C;
+      const int64_t ns = n_slices(q);
       for (int kvh = 0; kvh < H; ++kvh) {
-        int32_t grp = -1;
-        if (splits > 1) {
-          grp = (int32_t)(groups.size() / kGroupWords);
-          groups.push_back((int32_t)splits);
-          groups.push_back(n_slots);
-          groups.push_back((int32_t)ri);
-          groups.push_back(kvh);
-          n_slots += (int32_t)splits;
-        }
-        for (int64_t sp = 0; sp < splits; ++sp) {
-          Item& it = items[ni++];
-          const int64_t b0 = lo + sp * C, b1 = std::min<int64_t>(hi, b0 + C);
-          it.w[0] = q.role | kFlagChunk | (int32_t)(sp << kSplitShift);
-          it.w[1] = (int32_t)ri;
-          it.w[2] = kvh;
-          it.w[3] = 0;
-          it.w[4] = q.qo_len;
-          it.w[5] = (int32_t)b0;
-          it.w[6] = (int32_t)b1;
-          it.w[7] = grp;
-          it.cost = kChunkCostFixed + kChunkCostPerKey * (b1 - b0);
-          it.xcd = -1;
-        }
+        // one split group per row slice; a key range's slices are consecutive items
+        const int32_t grp0 = splits > 1 ? (int32_t)(groups.size() / kGroupWords) : -1;
+        if (splits > 1)
+          for (int64_t sl = 0; sl < ns; ++sl) {
+            groups.push_back((int32_t)splits);
+            groups.push_back(n_slots);
+            groups.push_back((int32_t)ri);
+            groups.push_back(kvh);
+            n_slots += (int32_t)splits;
+          }
+        for (int64_t sp = 0; sp < splits; ++sp)
+          for (int64_t sl = 0; sl < ns; ++sl) {
+            const int32_t grp = splits > 1 ? grp0 + (int32_t)sl : -1;
+            Item& it = items[ni++];
+            const int64_t b0 = lo + sp * C, b1 = std::min<int64_t>(hi, b0 + C);
+            it.w[0] = q.role | kFlagChunk | (int32_t)(sp << kSplitShift);
+            it.w[1] = (int32_t)ri;
+            it.w[2] = kvh;
+            it.w[3] = (int32_t)(sl * kChunkRows);   // first row (token x group) of the slice
+            it.w[4] = q.qo_len;
+            it.w[5] = (int32_t)b0;
+            it.w[6] = (int32_t)b1;
+            it.w[7] = grp;
+            it.cost = kChunkCostFixed + kChunkCostPerKey * (b1 - b0);
+            it.xcd = -1;
+          }
       }
     } else {
       for (int t0 = 0; t0 < q.qo_len; t0 += T) {
@@ -311,12 +319,25 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
       it.xcd = x;
       load[x] += it.cost;
     }
+    // key chunks: the least loaded die, heaviest first; the row slices of one
+    // (request, kv head, key range) share a die, so all but the first find
+    // their K/V in its L2 (the slices of a key range are consecutive items)
+    std::vector<uint32_t> pos(items.size());
+    for (size_t k = 0; k < order.size(); ++k) pos[order[k]] = (uint32_t)k;
     for (uint32_t i : order) {
       Item& it = items[i];
       if (!(it.w[0] & kFlagChunk)) continue;
-      int x = 0;
-      for (int y = 1; y < kNumXcds; ++y)
-        if (load[y] < load[x]) x = y;
+      int x = -1;
+      if (it.w[3] > 0) {
+        // slice 0 of this key range: the item w[3] / 32 places earlier
+        const size_t i0 = i - (size_t)(it.w[3] / kChunkRows);
+        if (items[i0].xcd >= 0 && pos[i0] < pos[i]) x = items[i0].xcd;
+      }
+      if (x < 0) {
+        x = 0;
+        for (int y = 1; y < kNumXcds; ++y)
+          if (load[y] < load[x]) x = y;
+      }
       it.xcd = x;
       load[x] += it.cost;
     }

@@ -1009,7 +1009,7 @@ __device__ __forceinline__ void fp8x16_widen(const u32x4 w, u32x4& c0, u32x4& c1
 // has at most 16 query rows (the wider form has no registers to spare).
 template <typename T, bool kFp8, int kCols>
 __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowGeom& rg, int kvh,
-                           int kv_begin, int kv_end, int split, int grp, char* lds, int wave_s,
+                           int row0, int kv_begin, int kv_end, int split, int grp, char* lds, int wave_s,
                            ChunkCarry& cc, bool& carried, int next_idx) {
   using V8 = typename Dt<T>::v8;
   // the thread index, rebuilt from the wave (scalar) and the lane count, so the
@@ -1023,10 +1023,12 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
   const int q16 = lane >> 4;                       // 16-column mode: lane group
   const int col = kCols == 16 ? (lane & 15) : r32;   // this lane's row of the item
   const int g = p.group_size;
-  const int rows = rg.qo_len * g;
+  // this item's rows: row0 .. row0 + rows - 1 of the request's q_len x group
+  // rows (a row slice of at most 32 when the request has more)
+  const int rows = min(kChunkRows, rg.qo_len * g - row0);
   const bool row_ok = col < rows;
-  const int tok = row_ok ? col / g : 0;
-  const int head = kvh * g + (row_ok ? col % g : 0);
+  const int tok = row_ok ? (row0 + col) / g : 0;
+  const int head = kvh * g + (row_ok ? (row0 + col) % g : 0);
 
   V8 qreg[8];
   if constexpr (kCols == 32) {
@@ -1351,8 +1353,8 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
   // final stage on the first 256 threads: row threadIdx / 8, 16 dims each
   const int frow = (tid >> 3) & 31, d0 = (tid & 7) * 16;
   const bool fok = tid < 256 && frow < rows;
-  const int ftok = fok ? frow / g : 0;
-  const int fhead = kvh * g + (fok ? frow % g : 0);
+  const int ftok = fok ? (row0 + frow) / g : 0;
+  const int fhead = kvh * g + (fok ? (row0 + frow) % g : 0);
   const int64_t out_row = (int64_t)(rg.qo_start + ftok);
   T* op = reinterpret_cast<T*>(r.out) + out_row * r.o_st + (int64_t)fhead * r.o_sh + d0;
   float* lse_p = r.lse ? r.lse + out_row * p.num_qo_heads + fhead : nullptr;
@@ -1480,7 +1482,7 @@ __device__ __forceinline__ int chunk_kind(PArg p, int idx) {
   CI32* it = plan_words(image_region(p, kHdrItems)) + idx * kItemWords;
   CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
   const bool fp8 = (it[0] & kFlagRole) && p.role[1].kv_fp8;
-  const bool narrow = rq[1] * p.group_size <= 16;
+  const bool narrow = rq[1] * p.group_size - it[3] <= 16;   // rows of the item (slice)
   return 2 * fp8 + narrow;
 }
 
@@ -1501,7 +1503,7 @@ __device__ __forceinline__ int chunk_items(PArg p, int idx0, int end, char* lds,
     const RoleView r = pick_role(p, flags & kFlagRole, kvh);
     CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
     const RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
-    chunk_item<T, kFp8, kCols>(p, r, rg, kvh, kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s,
+    chunk_item<T, kFp8, kCols>(p, r, rg, kvh, it[3], kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s,
                                cc, carried, next);
     if (next < 0) break;
     __syncthreads();   // the item is done with the LDS

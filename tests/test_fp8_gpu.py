@@ -43,6 +43,10 @@ CASES = [
     dict(ps=5, hqo=8, hkv=8, sinks=True),
     dict(hqo=32, hkv=4, dq=4, w=37, sinks=True),          # 32 rows per item, window, sinks
     dict(layout="HND", scales=(1.0, 1.0, 1.0), p_q=()),
+    # more than 32 rows per (request, kv head): key chunks in 32-row slices
+    dict(hqo=64, hkv=1, dq=1),                              # group 64: two slices
+    dict(hqo=16, hkv=2, dq=5, w=300, sinks=True),           # 8 x 5 = 40 rows: 32 + 8
+    dict(hqo=128, hkv=2, dq=2, ps=1, scales=(0.5, 2.0, 1.5)),  # 64 x 2 = 128 rows: four slices
 ]
 
 
@@ -76,10 +80,10 @@ def test_fp8_unit_scales_equal_bf16_of_same_values():
 def test_fp8_plan_checks():
     ws = torch.empty(16 << 20, dtype=torch.uint8, device="cuda")
     pod = BatchPOD(ws, "NHD", int_workspace_bytes=1 << 20)
-    # 64 rows per decode request (group 64): query tiles, which take no FP8
-    with pytest.raises(NotImplementedError, match="FP8"):
-        pod.plan(None, None, None, [0, 1], [0, 4], [16], num_qo_heads=64, num_kv_heads=1, head_dim=128,
-                 page_size=16, dtype=torch.bfloat16, kv_dtype_d=torch.float8_e4m3fn)
+    # 64 rows per decode request (group 64): planned as two 32-row key-chunk slices
+    pod.plan(None, None, None, [0, 1], [0, 4], [16], num_qo_heads=64, num_kv_heads=1, head_dim=128,
+             page_size=16, dtype=torch.bfloat16, kv_dtype_d=torch.float8_e4m3fn)
+    assert pod.plan_info()["n_decode_items"] == 2
     # no page table
     pod.plan(None, None, None, [0, 1], [0, 4], [16], num_qo_heads=8, num_kv_heads=1, head_dim=128,
              page_size=16, dtype=torch.bfloat16, kv_dtype_d=torch.float8_e4m3fn)

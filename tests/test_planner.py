@@ -13,7 +13,10 @@ FLAG_ROLE, FLAG_CHUNK = 1, 2
 
 
 def check_coverage(img, roles, hqo, hkv):
-    """roles: list of (qo_lens, kv_lens, causal, window_left) for prefill then decode."""
+    """roles: list of (qo_lens, kv_lens, causal, window_left) for prefill then decode.
+    Coverage is counted per row (token t, group head j) = t * g + j of each
+    (request, kv head): a query tile covers all g rows of its tokens, a key
+    chunk the up to 32 rows from its first row (word 3) on."""
     g = hqo // hkv
     im = decode_image(img)
     reqs = im["reqs"]
@@ -42,28 +45,31 @@ def check_coverage(img, roles, hqo, hkv):
         role, causal, w = role_of_req[req]
         assert (flags & FLAG_ROLE) == role
         qo_len, kv_len = int(reqs[req][1]), int(reqs[req][2])
-        c = cover.setdefault((req, kvh), np.zeros((qo_len, kv_len), np.int32))
+        c = cover.setdefault((req, kvh), np.zeros((qo_len * g, kv_len), np.int32))
         if flags & FLAG_CHUNK:
-            assert tok0 == 0 and ntok == qo_len and qo_len * g <= 32
-            rows = range(qo_len)
+            # tok0 holds the first row of the item's slice
+            assert ntok == qo_len and tok0 % 32 == 0 and 0 <= tok0 < qo_len * g
+            rows = range(tok0, min(tok0 + 32, qo_len * g))
             if grp >= 0:
                 group_members.setdefault(grp, []).append(flags >> 8)
+                assert int(im["groups"][grp][2]) == req and int(im["groups"][grp][3]) == kvh
         else:
             assert ntok * g <= 256 and grp == -1
-            rows = range(tok0, tok0 + ntok)
+            rows = range(tok0 * g, (tok0 + ntok) * g)
         assert 0 <= kb < ke <= kv_len
-        for i in rows:
-            p = kv_len - qo_len + i
+        for r in rows:
+            p = kv_len - qo_len + r // g
             lo = max(0, p - w) if w >= 0 else 0
             hi = p if causal else kv_len - 1
             # every valid key of the row inside the item's range is counted once
-            c[i, max(kb, lo):min(ke, hi + 1)] += 1
+            c[r, max(kb, lo):min(ke, hi + 1)] += 1
     assert n_real == im["n_items"]
     for (req, kvh), c in cover.items():
         role, causal, w = role_of_req[req]
-        qo_len, kv_len = c.shape
-        for i in range(qo_len):
-            p = kv_len - qo_len + i
+        kv_len = c.shape[1]
+        qo_len = c.shape[0] // g
+        for i in range(qo_len * g):
+            p = kv_len - qo_len + i // g
             lo = max(0, p - w) if w >= 0 else 0
             hi = p if causal else kv_len - 1
             assert np.all(c[i, lo:hi + 1] == 1), (req, kvh, i)
@@ -348,3 +354,42 @@ def test_workspace_query_of_long_single_decodes(hq, hk, kv_len):
     assert fb == info.float_ws_bytes == info.n_slots * (32 * 128 + 32) * 4
     assert ib == info.int_ws_bytes
     assert info.n_groups > 0 and fb > 16 << 20
+
+
+@pytest.mark.parametrize("chunk", [0, 64, -1])
+@pytest.mark.parametrize("hqo,hkv,q_lens", [(64, 1, [1, 2, 1]), (64, 8, [5, 4, 1]), (128, 1, [1, 3])])
+def test_fp8_decode_row_slices(hqo, hkv, q_lens, chunk):
+    """An FP8 decode cache puts requests with more than 32 rows (q_len x group)
+    into key chunks of 32-row slices: coverage stays exact, each slice of a
+    split key range has a split group of its own, and the slices of one key
+    range are consecutive items on one die."""
+    kv = [300 + 700 * i for i in range(len(q_lens))]
+    roles = [([70], [300], True, -1), (q_lens, kv, True, -1)]
+    desc, keep = plan_desc(prefill=dict(qo_lens=roles[0][0], kv_lens=roles[0][1]),
+                           decode=dict(qo_lens=q_lens, kv_lens=kv), hqo=hqo, hkv=hkv, decode_chunk=chunk)
+    desc.decode_kv_dtype = _lib.POD_DTYPE_FP8_E4M3
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    im = check_coverage(img, roles, hqo, hkv)
+    g = hqo // hkv
+    items = [it for it in im["items"]]
+    dec_chunks = [i for i, it in enumerate(items) if int(it[0]) & FLAG_CHUNK and int(it[0]) & FLAG_ROLE]
+    assert dec_chunks and all(int(items[i][0]) & FLAG_CHUNK for i in range(len(items))
+                              if int(items[i][0]) & FLAG_ROLE)
+    assert max(int(items[i][3]) for i in dec_chunks) >= 32
+    # slices of one key range share a die (workgroup w runs on die w % 8)
+    die = {}
+    for i in dec_chunks:
+        it = items[i]
+        w = int(im["wg_of_item"][i])
+        if w < 0:
+            continue          # shared pool: any workgroup
+        die.setdefault((int(it[1]), int(it[2]), int(it[5])), set()).add(w % 8)
+    assert all(len(v) == 1 for v in die.values())
+
+
+def test_bf16_large_group_decode_still_uses_tiles():
+    desc, keep = plan_desc(decode=dict(qo_lens=[1, 2], kv_lens=[100, 300]), hqo=64, hkv=1)
+    rc, img, info = compute(desc)
+    im = decode_image(img)
+    assert not any(int(it[0]) & FLAG_CHUNK for it in im["items"])
