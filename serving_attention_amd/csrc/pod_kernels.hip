@@ -650,14 +650,17 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
         }
         ow[db][b] = u32x4{P[0], P[1], Q[0], Q[1]};
       }
+    // outputs are written once and not read again in the launch: non-temporal
+    // stores stream them out now instead of leaving dirty lines in L2 for the
+    // write-back at the end of the launch
     if (ok) {
       T* op = reinterpret_cast<T*>(r.out) + (int64_t)(d.qrow0 + toff) * r.o_st + (int64_t)head * r.o_sh + hi * 8;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) *reinterpret_cast<u32x4*>(op + db * 32 + 16 * b) = ow[db][b];
+        for (int b = 0; b < 2; ++b) __builtin_nontemporal_store(ow[db][b], reinterpret_cast<u32x4*>(op + db * 32 + 16 * b));
       if (r.lse && hi == 0)
-        r.lse[(int64_t)(d.qrow0 + toff) * q.num_qo_heads + head] = lt > 0.f ? mu2 + fast_log2(lt) : kNegInf;
+        __builtin_nontemporal_store(lt > 0.f ? mu2 + fast_log2(lt) : kNegInf, &r.lse[(int64_t)(d.qrow0 + toff) * q.num_qo_heads + head]);
     }
   };
 
@@ -1385,9 +1388,9 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
         w0[i] = (T)(vals[i] * inv);
         w1[i] = (T)(vals[8 + i] * inv);
       }
-      reinterpret_cast<u32x4*>(op)[0] = __builtin_bit_cast(u32x4, w0);
-      reinterpret_cast<u32x4*>(op)[1] = __builtin_bit_cast(u32x4, w1);
-      if (lse_p && (tid & 7) == 0) *lse_p = lse_r;
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, w0), reinterpret_cast<u32x4*>(op));
+      __builtin_nontemporal_store(__builtin_bit_cast(u32x4, w1), reinterpret_cast<u32x4*>(op) + 1);
+      if (lse_p && (tid & 7) == 0) __builtin_nontemporal_store(lse_r, lse_p);
     } else {
       const int first_slot = image_region(p, kHdrGroups)[grp * kGroupWords + 1];
       float* slot = p.partials + (int64_t)(first_slot + split) * kSlotFloats;
@@ -1469,9 +1472,9 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
       w0[i] = (T)(acc16[i] * inv);
       w1[i] = (T)(acc16[8 + i] * inv);
     }
-    reinterpret_cast<u32x4*>(op)[0] = __builtin_bit_cast(u32x4, w0);
-    reinterpret_cast<u32x4*>(op)[1] = __builtin_bit_cast(u32x4, w1);
-    if (lse_p && (tid & 7) == 0) *lse_p = L;
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, w0), reinterpret_cast<u32x4*>(op));
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, w1), reinterpret_cast<u32x4*>(op) + 1);
+    if (lse_p && (tid & 7) == 0) __builtin_nontemporal_store(L, lse_p);
   }
   if (tid == 0) atomicExch(image_region(p, kHdrCounters) + grp, 0);
 }
