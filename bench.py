@@ -30,6 +30,8 @@ METRIC = "POD step latency (µs); prefill TFLOP/s + decode KV HBM GB/s vs roofli
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 / fp16 MFMA
 KERNEL_NAME = "pod_grid_kernel"
+# GPU spin ahead of each timed launch (about 100 us at the shader clock)
+SPIN_CYCLES = 200_000
 
 DESCR = {
     "single_decode": "single-request decode: q [32,128] fp16, K/V [2048,32,128] fp16, NHD",
@@ -155,7 +157,10 @@ def alloc_outs(w, roles):
 
 
 def time_kernel(pod, layers, roles, steps, warmup, decode_chunk, order, replan):
-    """Mean launch duration (HIP events on the launch stream) and mean wall step time."""
+    """Mean wall time per step (plan + launch, GPU kept busy), the launch
+    durations inside that timed region (HIP events on the launch stream), and
+    the launch durations measured apart with each launch queued ahead of its
+    start event."""
     import torch
     outs = [alloc_outs(w, roles) for w in layers]
     plan(pod, layers[0], roles, decode_chunk, order)
@@ -182,8 +187,24 @@ def time_kernel(pod, layers, roles, steps, warmup, decode_chunk, order, replan):
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern = [a.elapsed_time(b) * 1e3 for a, b in ev]   # us
-    kern.sort()
+    kern = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)   # us
+    # A launch shorter than the host's plan + argument marshalling leaves the
+    # GPU idle between steps, and then a start event can fire before its launch
+    # is queued. Here each launch (after its plan, as in a step) waits behind a
+    # short GPU spin recorded ahead of the start event, so only the launch
+    # itself is timed.
+    ev2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        w = layers[i % len(layers)]
+        if replan:
+            plan(pod, w, roles, decode_chunk, order)
+        torch.cuda._sleep(SPIN_CYCLES)
+        ev2[i][0].record(stream)
+        run(pod, w, roles, outs[i % len(layers)])
+        ev2[i][1].record(stream)
+    torch.cuda.synchronize()
+    spaced = sorted(a.elapsed_time(b) * 1e3 for a, b in ev2)
     # In the loop, plan() also waits for the launch that last read the
     # workspace half it writes (the host runs ahead of the GPU). Its own cost
     # is timed apart, with the GPU idle, after the timed region.
@@ -198,8 +219,10 @@ def time_kernel(pod, layers, roles, steps, warmup, decode_chunk, order, replan):
             tp += time.perf_counter() - t
         plan_cost = tp / n * 1e6
     return dict(step_us=wall / steps * 1e6, kernel_us=sum(kern) / len(kern),
-                kernel_p10_us=kern[len(kern) // 10], kernel_p50_us=kern[len(kern) // 2],
+                kernel_p10_us=kern[len(kern) // 10],
                 kernel_p90_us=kern[min(len(kern) - 1, (9 * len(kern)) // 10)],
+                kernel_spaced_us=sum(spaced) / len(spaced),
+                kernel_spaced_p50_us=spaced[len(spaced) // 2],
                 plan_us=plan_cost,
                 plan_in_loop_us=plan_s / steps * 1e6 if replan else None)
 
@@ -436,8 +459,8 @@ def graph_bench(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="pod_chunked", choices=sorted(DESCR))
     ap.add_argument("--layers", type=int, default=None,
                     help="distinct KV caches / queries cycled per step (default: 4, 1 for pod_chunked)")
@@ -509,6 +532,7 @@ def main():
             wk = work[name]
             roles_out[name] = dict(
                 kernel_us=t["kernel_us"],
+                kernel_spaced_us=t["kernel_spaced_us"],
                 tflops=wk["flops"] / (t["kernel_us"] * 1e-6) / 1e12,
                 kv_gbs=wk["kv_bytes"] / (t["kernel_us"] * 1e-6) / 1e9,
                 hbm_gbs=(wk["kv_bytes"] + wk["io_bytes"]) / (t["kernel_us"] * 1e-6) / 1e9)
@@ -548,6 +572,8 @@ def main():
         "kernel_us": k_us,
         "kernel_p10_us": main_t["kernel_p10_us"],
         "kernel_p90_us": main_t["kernel_p90_us"],
+        "kernel_spaced_us": main_t["kernel_spaced_us"],
+        "kernel_spaced_p50_us": main_t["kernel_spaced_p50_us"],
         "plan_us": main_t["plan_us"],
         "plan_in_loop_us": main_t["plan_in_loop_us"],
         "prefill_tflops": flops_p / (k_us * 1e-6) / 1e12 if flops_p else None,
