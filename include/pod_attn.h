@@ -201,7 +201,9 @@ typedef struct pod_plan_info {
   int32_t n_decode_items;
   int32_t n_groups;         /* split (request, kv head) units that need the LSE merge */
   int32_t n_slots;          /* partial-state slots in the float workspace */
-  int32_t grid;             /* persistent workgroups launched (one per CU) */
+  int32_t grid;             /* persistent workgroups launched: one per CU, or, for a
+                               plan with fewer items than CUs (outside graph mode),
+                               one per item rounded up to a multiple of 8 */
   int32_t decode_chunk;     /* keys per decode split actually used */
   int32_t image_ints;       /* int32 words of the work-list image */
   int64_t float_ws_bytes;   /* float workspace the plan needs */
@@ -339,8 +341,11 @@ const char* pod_last_error(void);
  * float_ws_bytes for split-KV partial states, int_ws_bytes for the work list
  * (two alternating images). The pages recommend a 128 MB float workspace
  * ([POD] "使用建议与已知限制"); this query gives the exact need, which grows with
- * the number of split decode chunks. Either output pointer may be NULL.
- * Errors as pod_plan's validation (POD_ERR_INVALID / POD_ERR_UNSUPPORTED).
+ * the number of split decode chunks. The sizes are those of a full grid (one
+ * workgroup per CU, as a graph-mode context keeps), an upper bound for the
+ * smaller grid pod_plan gives a plan with few items. Either output pointer may
+ * be NULL. Errors as pod_plan's validation (POD_ERR_INVALID /
+ * POD_ERR_UNSUPPORTED).
  */
 int pod_workspace_bytes(const pod_plan_desc* desc, size_t* float_ws_bytes,
                         size_t* int_ws_bytes);
@@ -400,7 +405,8 @@ int pod_run_static(const pod_plan_desc* desc, const pod_run_args* args, int devi
  *     items, from pool_first on, are key chunks that any workgroup takes from a
  *     shared queue once its own list is done.
  *   tdesc[n_items][8]: per query tile {first query row, tokens, kv head, diagonal
- *     key of the first token, key end, kv_len, 0, 0}; zero for key chunks.
+ *     key of the first token, key end, kv_len, 0, 0}; per key chunk its request's
+ *     {qo_start, qo_len, kv_len, page_start, 0, 0, 0, 0}.
  *   wgs[grid][8]: per persistent workgroup {first item, query tiles, key chunks,
  *     first block, blocks, chunks run first (0/1), prefill-role tiles, blocks of
  *     those}. Workgroup w runs on die w % 8.

@@ -115,7 +115,7 @@ int validate_role(const pod_role_desc& r, const char* name, int page_size, std::
 }  // namespace
 
 int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& info,
-                 std::string* err) {
+                 std::string* err, bool fixed_grid) {
   info = pod_plan_info{};
   if (d.num_qo_heads <= 0 || d.num_kv_heads <= 0)
     return fail(err, POD_ERR_INVALID, "num_qo_heads and num_kv_heads must be positive");
@@ -343,8 +343,19 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
     }
   }
 
-  // The shared pool: the lightest key chunks, up to kPoolShare of their cost.
-  const int G = num_cus;
+  // Workgroups: one per CU; or, when every die's items fit one workgroup each
+  // and the grid need not stay fixed, as many per die as the most items a die
+  // holds, so a small step launches few idle workgroups.
+  int G = num_cus;
+  if (!fixed_grid) {
+    int64_t per_die[kNumXcds] = {};
+    for (const Item& it : items) ++per_die[it.xcd];
+    const int64_t most = std::max<int64_t>(1, *std::max_element(per_die, per_die + kNumXcds));
+    if (most * kNumXcds < num_cus) G = (int)(most * kNumXcds);
+  }
+  // The shared pool: the lightest key chunks, up to kPoolShare of their cost
+  // (none when every item has a workgroup of its own).
+  const bool use_pool = G > 1 && items.size() > (size_t)G;
   std::vector<uint8_t> in_pool(items.size(), 0);
   std::vector<uint32_t> pool;
   {
@@ -353,7 +364,7 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
       if (it.w[0] & kFlagChunk) chunk_cost += it.cost;
     const int64_t budget = (int64_t)(kPoolShare * (double)chunk_cost);
     int64_t taken = 0;
-    for (size_t k = order.size(); k-- > 0 && G > 1;) {   // lightest first
+    for (size_t k = order.size(); k-- > 0 && use_pool;) {   // lightest first
       const Item& it = items[order[k]];
       if (!(it.w[0] & kFlagChunk)) continue;
       if (taken + it.cost > budget) break;
@@ -460,6 +471,26 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
     q[2] = reqs[i].kv_len;
     q[3] = reqs[i].page_start;
   }
+  // Per-item row beside the item, read with it: a query tile's boundary data
+  // (what an item boundary needs, without the request table); a key chunk's
+  // request fields (so its loads need no request-table round trip).
+  auto write_tdesc = [&](int32_t* td, const Item& it) {
+    for (int x = 0; x < kTdescWords; ++x) td[x] = 0;
+    const Req& q = reqs[it.w[1]];
+    if (it.w[0] & kFlagChunk) {
+      td[0] = q.qo_start;
+      td[1] = q.qo_len;
+      td[2] = q.kv_len;
+      td[3] = q.page_start;
+    } else {
+      td[0] = q.qo_start + it.w[3];
+      td[1] = it.w[4];
+      td[2] = it.w[2];
+      td[3] = q.kv_len - q.qo_len + it.w[3];
+      td[4] = it.w[6];
+      td[5] = q.kv_len;
+    }
+  };
   int n_pre = 0, n_dec = 0;
   int64_t k = 0, blk = 0;
   for (int w = 0; w < G; ++w) {
@@ -512,18 +543,7 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
       const Item& it = items[tl[j]];
       int32_t* dst = h + items_off + k * kItemWords;
       for (int x = 0; x < kItemWords; ++x) dst[x] = it.w[x];
-      // query tiles: what an item boundary needs, without the request table
-      int32_t* td = h + tdesc_off + k * kTdescWords;
-      for (int x = 0; x < kTdescWords; ++x) td[x] = 0;
-      if (!(it.w[0] & kFlagChunk)) {
-        const Req& q = reqs[it.w[1]];
-        td[0] = q.qo_start + it.w[3];
-        td[1] = it.w[4];
-        td[2] = it.w[2];
-        td[3] = q.kv_len - q.qo_len + it.w[3];
-        td[4] = it.w[6];
-        td[5] = q.kv_len;
-      }
+      write_tdesc(h + tdesc_off + k * kTdescWords, it);
       ++k;
       ++((it.w[0] & kFlagRole) ? n_dec : n_pre);
     }
@@ -532,7 +552,7 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
     const Item& it = items[i];
     int32_t* dst = h + items_off + k * kItemWords;
     for (int j = 0; j < kItemWords; ++j) dst[j] = it.w[j];
-    for (int j = 0; j < kTdescWords; ++j) h[tdesc_off + k * kTdescWords + j] = 0;
+    write_tdesc(h + tdesc_off + k * kTdescWords, it);
     ++k;
     ++((it.w[0] & kFlagRole) ? n_dec : n_pre);
   }

@@ -235,7 +235,7 @@ int pod_plan_compute(const pod_plan_desc* desc, int32_t* image, size_t image_cap
   int rc = pod::plan_compute(*desc, [&](size_t n) -> int32_t* {
     fits = image != nullptr && n <= image_cap;
     return fits ? image : nullptr;
-  }, inf, &err);
+  }, inf, &err, false);
   if (rc) return set_err(rc, err);
   if (info) *info = inf;
   if (!fits) return set_err(POD_ERR_WORKSPACE, "image buffer too small for the plan");
@@ -247,7 +247,7 @@ int pod_workspace_bytes(const pod_plan_desc* desc, size_t* float_ws_bytes, size_
   if (!desc) return set_err(POD_ERR_INVALID, "desc is NULL");
   pod_plan_info inf;
   std::string err;
-  int rc = pod::plan_compute(*desc, nullptr, inf, &err);
+  int rc = pod::plan_compute(*desc, nullptr, inf, &err, true);   // the larger image
   if (rc) return set_err(rc, err);
   if (float_ws_bytes) *float_ws_bytes = (size_t)inf.float_ws_bytes;
   if (int_ws_bytes) *int_ws_bytes = (size_t)inf.int_ws_bytes;
@@ -375,7 +375,7 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   };
   pod_plan_info inf;
   std::string err;
-  int rc = pod::plan_compute(d, sink, inf, &err);
+  int rc = pod::plan_compute(d, sink, inf, &err, ctx->graph);
   if (rc) return set_err(rc, err);
   if (what) return hip_err(e, what);
   // graph mode keeps one image; otherwise two alternate
@@ -559,7 +559,7 @@ int pod_run_static(const pod_plan_desc* desc, const pod_run_args* args, int devi
     words = n;
     fits = n * sizeof(int32_t) <= pod::kStaticImageBytes;
     return fits ? g_static_image : nullptr;
-  }, inf, &err);
+  }, inf, &err, false);
   if (rc) return set_err(rc, err);
   if (!fits)
     return set_err(POD_ERR_WORKSPACE, "work list of " + std::to_string(words * 4) +

@@ -25,9 +25,10 @@ constexpr int kNumXcds = 8;            // MI355X: 8 accelerator dies, 32 CUs eac
 constexpr int kSlotFloats = kChunkRows * kHeadDim + kChunkRows;   // partial O + LSE
 constexpr int kWgWords = 8;            // per-workgroup list header
 constexpr int kBlockWords = 4;         // query-tile block-table entry
-// Per-item boundary data of a query tile, parallel to the items:
+// Per-item row parallel to the items. A query tile's boundary data:
 //   {first query row (qo_start + tok0), tokens, kv head, diagonal key of the
-//    first token (kv_len - qo_len + tok0), key end of the item, kv_len, 0, 0}
+//    first token (kv_len - qo_len + tok0), key end of the item, kv_len, 0, 0};
+// a key chunk's request fields: {qo_start, qo_len, kv_len, page_start, 0, 0, 0, 0}
 constexpr int kTdescWords = 8;
 constexpr int kMaxSinkHeads = 1024;    // sinks staged in LDS by the query tiles
 constexpr int kMaxKvHeads = 16384;     // kv head index fits the block-table entry
@@ -97,9 +98,13 @@ struct Params {
 // Host planner (planner.cpp). It validates `d`, fills `info`, and asks `sink`
 // for a buffer of info.image_ints words to write the work-list image into; a
 // null sink, or a sink that returns nullptr, computes the sizes only.
+// fixed_grid: launch d.num_cus workgroups whatever the plan holds (a captured
+// launch keeps its grid across plans); otherwise a plan with fewer items than
+// CUs gets one workgroup per item, rounded up to a multiple of the die count.
+// The fixed grid's image is the larger one (the sizes to reserve).
 using ImageSink = std::function<int32_t*(size_t)>;
 int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& info,
-                 std::string* err);
+                 std::string* err, bool fixed_grid);
 
 // Launch the fused grid on `stream` (a hipStream_t); `done_event` (a hipEvent_t,
 // or null) is signalled when the launch completes. Returns a hipError_t value.

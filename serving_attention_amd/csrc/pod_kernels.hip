@@ -1179,8 +1179,8 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
       const int nfirst = it[5] + kStepKeys * wave_s;
       if (nfirst < it[6]) {
         const RoleView r2 = pick_role(p, it[0] & kFlagRole, it[2]);
-        CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
-        nxt = KeySrc{r2.k, r2.v, r2.indices, r2.kv_sp_b, r2.kv_st_b, rq[3], nfirst, it[6] - 1};
+        CI32* td = plan_words(image_region(p, kHdrTdesc)) + next_idx * kTdescWords;
+        nxt = KeySrc{r2.k, r2.v, r2.indices, r2.kv_sp_b, r2.kv_st_b, td[3], nfirst, it[6] - 1};
         has_next = true;
       }
     }
@@ -1483,9 +1483,9 @@ __device__ __forceinline__ void chunk_item(PArg p, const RoleView& r, const RowG
 // MFMAs).
 __device__ __forceinline__ int chunk_kind(PArg p, int idx) {
   CI32* it = plan_words(image_region(p, kHdrItems)) + idx * kItemWords;
-  CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
+  CI32* td = plan_words(image_region(p, kHdrTdesc)) + idx * kTdescWords;   // request fields
   const bool fp8 = (it[0] & kFlagRole) && p.role[1].kv_fp8;
-  const bool narrow = rq[1] * p.group_size - it[3] <= 16;   // rows of the item (slice)
+  const bool narrow = td[1] * p.group_size - it[3] <= 16;   // rows of the item (slice)
   return 2 * fp8 + narrow;
 }
 
@@ -1504,8 +1504,8 @@ __device__ __forceinline__ int chunk_items(PArg p, int idx0, int end, char* lds,
     const int flags = it[0];
     const int kvh = it[2], kv_begin = it[5], kv_end = it[6], grp = it[7];
     const RoleView r = pick_role(p, flags & kFlagRole, kvh);
-    CI32* rq = plan_words(image_region(p, kHdrReqs)) + it[1] * kReqWords;
-    const RowGeom rg{rq[0], rq[1], rq[2], rq[3]};
+    CI32* td = plan_words(image_region(p, kHdrTdesc)) + idx * kTdescWords;   // request fields
+    const RowGeom rg{td[0], td[1], td[2], td[3]};
     chunk_item<T, kFp8, kCols>(p, r, rg, kvh, it[3], kv_begin, kv_end, flags >> kSplitShift, grp, lds, wave_s,
                                cc, carried, next);
     if (next < 0) break;

@@ -2,6 +2,8 @@
 every (row, kv head, valid key) exactly once, split groups are consistent, the
 per-workgroup lists partition the items and their block tables match the query
 tiles, and bad inputs get their error code."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -203,8 +205,15 @@ def test_workgroup_lists(wl, order):
     assert rc == _lib.POD_OK
     im = decode_image(img)
     items, wgs = im["items"], im["wgs"]
-    assert info.grid == 256 and len(wgs) == 256
+    # one workgroup per CU, or, when every die's items fit one workgroup each,
+    # as many per die as the busiest die has items (workgroup w runs on die w % 8)
+    assert len(wgs) == info.grid and info.grid % 8 == 0 and info.grid <= 256
     pf, pc = im["pool_first"], im["pool_count"]
+    if info.grid < 256:
+        per_wg = [int(wg[1]) + int(wg[2]) for wg in wgs]
+        assert pc == 0 and max(per_wg) <= 1
+        busy = [sum(per_wg[x::8]) for x in range(8)]
+        assert info.grid == 8 * max(1, max(busy))
     assert pf + pc == im["n_items"]
     assert np.all(im["wg_of_item"][:pf] >= 0) and np.all(im["wg_of_item"][pf:] == -1)
     nxt = 0
@@ -274,14 +283,35 @@ def test_block_tables(wl):
         total += nb
     assert total == len(blocks)
     # each query tile's boundary row: first query row, tokens, kv head, diagonal
-    # key of its first token, key end, kv_len; zero rows for key chunks
+    # key of its first token, key end, kv_len; a key chunk's row: its request's
+    # qo_start, qo_len, kv_len, page_start
     for it, td in zip(items, im["tdesc"]):
         if int(it[0]) & FLAG_CHUNK:
-            assert not td.any()
+            assert [int(x) for x in td] == [int(x) for x in reqs[int(it[1])]] + [0, 0, 0, 0]
             continue
         qs, ql, kl = (int(x) for x in reqs[int(it[1])][:3])
         assert [int(x) for x in td] == [qs + int(it[3]), int(it[4]), int(it[2]),
                                         kl - ql + int(it[3]), int(it[6]), kl, 0, 0]
+
+
+@pytest.mark.parametrize("batch", [1, 3, 20, 40])
+def test_small_plans_get_one_workgroup_per_item(batch):
+    """A plan with fewer items than CUs launches one workgroup per item, rounded
+    up to whole dies, and no shared pool; the workspace query reserves the image
+    of the full grid, which is larger."""
+    desc, keep = plan_desc(decode=dict(qo_lens=[1] * batch, kv_lens=[300] * batch), hqo=16, hkv=2,
+                           decode_chunk=-1)
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    n = 2 * batch   # equal items: the dies take turns
+    assert info.n_items == n and info.grid == max(8, -(-n // 8) * 8)
+    im = decode_image(img)
+    assert im["pool_count"] == 0
+    assert sorted(int(wg[1]) + int(wg[2]) for wg in im["wgs"]) == [0] * (info.grid - n) + [1] * n
+    check_coverage(img, [([], [], True, -1), ([1] * batch, [300] * batch, True, -1)], 16, 2)
+    fb, ib = ctypes.c_size_t(), ctypes.c_size_t()
+    assert _lib.load().pod_workspace_bytes(ctypes.byref(desc), ctypes.byref(fb), ctypes.byref(ib)) == 0
+    assert ib.value == 2 * (-(-(info.image_ints + 8 * (256 - info.grid)) * 4 // 256) * 256)
 
 
 def test_workspace_sizes():
