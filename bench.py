@@ -456,6 +456,86 @@ def graph_bench(args):
     }))
 
 
+def _smi_sample():
+    """(socket power W, graphics clock MHz) from one amd-smi reading, or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-p", "-c"], capture_output=True, text=True, timeout=5)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    pw = re.search(r"SOCKET_POWER:\s*(\d+)", r.stdout)
+    gfx = r.stdout.find("GFX_0")
+    clk = re.search(r"\n\s+CLK:\s*(\d+)\s*MHz", r.stdout[gfx:]) if gfx >= 0 else None
+    if not pw or not clk:
+        return None
+    return int(pw.group(1)), int(clk.group(1))
+
+
+def power_bench(args):
+    """Board power and graphics clock while each role set of --workload runs
+    launch after launch (no planning between them) for --power-secs seconds,
+    and for an idle stretch: amd-smi readings in a thread beside the launches.
+    Energy per launch = mean power x launch time."""
+    import threading
+    import torch
+    from serving_attention_amd import BatchPOD
+    w = make_layers(args.workload, 1, "cuda")[0]
+    ws = torch.empty(128 << 20, dtype=torch.uint8, device="cuda")
+    pod = BatchPOD(ws, w.spec.kv_layout, int_workspace_bytes=8 << 20)
+    all_roles = tuple(n for n, _ in w.roles())
+    sets = [(r,) for r in all_roles] + ([all_roles] if len(all_roles) == 2 else []) + [()]
+    res = {}
+    for roles in sets:
+        name = "+".join(roles) or "idle"
+        samples, stop = [], threading.Event()
+
+        def sampler():
+            time.sleep(0.3)   # let the clock settle
+            while not stop.is_set():
+                x = _smi_sample()
+                if x:
+                    samples.append(x)
+        if roles:
+            outs = alloc_outs(w, roles)
+            plan(pod, w, roles, args.decode_chunk, args.order)
+            for _ in range(5):
+                run(pod, w, roles, outs)
+            torch.cuda.synchronize()
+        th = threading.Thread(target=sampler)
+        th.start()
+        n, t0 = 0, time.perf_counter()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        while time.perf_counter() - t0 < args.power_secs:
+            if roles:
+                for _ in range(20):
+                    run(pod, w, roles, outs)
+                n += 20
+                torch.cuda.synchronize()
+            else:
+                time.sleep(0.05)
+        ev1.record()
+        torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        us = ev0.elapsed_time(ev1) * 1e3 / n if n else None
+        pw = [p for p, _ in samples]
+        ck = [c for _, c in samples]
+        res[name] = dict(launches=n, us_per_launch=us, samples=len(samples),
+                         power_w=sum(pw) / len(pw) if pw else None, power_w_max=max(pw) if pw else None,
+                         gfx_mhz=sum(ck) / len(ck) if ck else None,
+                         mj_per_launch=(sum(pw) / len(pw)) * us * 1e-3 if pw and us else None)
+        print(json.dumps({"mode": name, **res[name]}), file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "board power (W) and graphics clock (MHz) per role set, launches back to back",
+        "value": res.get("+".join(all_roles), {}).get("power_w"), "unit": "W", "higher_is_better": False,
+        "n_gpus": 1, "dtype": w.spec.dtype, "data": "synthetic",
+        "config": {"workload": args.workload, "seconds_per_mode": args.power_secs},
+        "modes": res,
+    }))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -476,6 +556,10 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time per-layer eager run() calls against replays of one captured graph "
                          "(graph-mode context) on --workload")
+    ap.add_argument("--power", action="store_true",
+                    help="board power and graphics clock (amd-smi) while each role set of --workload "
+                         "runs launch after launch, and idle")
+    ap.add_argument("--power-secs", type=float, default=4.0)
     ap.add_argument("--cascade", action="store_true",
                     help="time the two-level shared-prefix cascade (one launch + merge) "
                          "against the one-level decode over the same keys")
@@ -491,6 +575,9 @@ def main():
 
     if args.cascade:
         cascade_bench(args)
+        return
+    if args.power:
+        power_bench(args)
         return
     if args.graph:
         graph_bench(args)
