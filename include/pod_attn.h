@@ -263,8 +263,11 @@ int pod_destroy(pod_ctx_t ctx);
  *   workspace. The copy runs on a stream the context owns, once the launches of
  *   the plan before last (which read the same half) have finished (the host
  *   waits for them only if they are still running), so it overlaps the
- *   previous plan's launches; pod_plan then waits on the host for that copy
- *   alone (a few microseconds), so pod_run needs no stream-ordering of its own.
+ *   previous plan's launches. While the previous plan's launch still runs,
+ *   pod_plan then waits on the host for that copy alone (a few microseconds),
+ *   so pod_run enqueues its launch without a cross-stream wait; when the GPU is
+ *   idle pod_plan returns at once and pod_run orders its launch after the copy
+ *   on the device.
  *   The first copy into each half is also ordered after the work queued on
  *   `stream` when pod_plan is called (so a caller that initialises int_ws on
  *   `stream` just before, or still uses that memory there, is safe); pod_plan

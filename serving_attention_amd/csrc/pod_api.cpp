@@ -435,13 +435,30 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (work list)");
   e = hipEventRecord(ctx->staged[k], ctx->copy_stream);
   if (e != hipSuccess) return hip_err(e, "hipEventRecord");
-  // The host waits for this copy (a few microseconds on the library's own
-  // stream; launches already queued keep running), so pod_run enqueues the
-  // launch alone: a cross-stream wait ahead of each launch measured 2-5 us
-  // slower per step.
-  e = hipEventSynchronize(ctx->staged[k]);
-  if (e != hipSuccess) return hip_err(e, "hipEventSynchronize");
-  ctx->staged_pending[k] = false;
+  // While the previous plan's launch still runs, the host waits for this copy
+  // behind it (a few microseconds; the launch keeps the GPU busy), so pod_run
+  // enqueues the next launch alone: a cross-stream wait ahead of each launch
+  // measured 2-5 us slower per step. With the GPU idle, that wait would only
+  // hold the host: pod_plan returns at once and pod_run orders its launch
+  // after the copy on the device.
+  bool gpu_busy = false;
+  if (ctx->used_pending[ctx->cur]) {
+    e = hipEventQuery(ctx->used[ctx->cur]);
+    if (e == hipSuccess) {
+      ctx->used_pending[ctx->cur] = false;
+    } else if (e == hipErrorNotReady) {
+      gpu_busy = true;
+    } else {
+      return hip_err(e, "hipEventQuery");
+    }
+  }
+  if (gpu_busy) {
+    e = hipEventSynchronize(ctx->staged[k]);
+    if (e != hipSuccess) return hip_err(e, "hipEventSynchronize");
+    ctx->staged_pending[k] = false;
+  } else {
+    ctx->staged_pending[k] = true;
+  }
   ctx->cur = k;
   ctx->next_staging = 1 - k;
   }
@@ -481,8 +498,8 @@ int pod_run(pod_ctx_t ctx, const pod_run_args* args, void* stream) {
     g_err.clear();
     return POD_OK;
   }
-  // this plan's work list must be up (pod_plan waited for its copy; the
-  // stream wait stays for safety and is not taken)
+  // this plan's work list must be up: pod_plan waited for its copy when the
+  // GPU was busy; otherwise the launch waits for it on the device
   hipError_t he = hipSuccess;
   if (ctx->staged_pending[ctx->cur]) {
     he = hipEventQuery(ctx->staged[ctx->cur]);
