@@ -380,9 +380,20 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
   // of its workgroups (LPT), so every workgroup holds a static list.
   // Per die a min-heap of (load, workgroup); ties go to the lower workgroup.
   std::vector<int32_t> wg_of(items.size(), -1);
-  {
+  if (G < num_cus) {
+    // every die's items fit one workgroup each: the heap below would hand die
+    // x's items, in order, to its workgroups x, x + 8, ... (all still empty)
+    int32_t next[kNumXcds];
+    for (int x = 0; x < kNumXcds; ++x) next[x] = x;
+    for (uint32_t i : order) {
+      const int x = items[i].xcd;
+      wg_of[i] = next[x];
+      next[x] += kNumXcds;
+    }
+  } else {
     using Slot = std::pair<int64_t, int32_t>;
     std::vector<Slot> heap[kNumXcds];
+    for (int x = 0; x < kNumXcds; ++x) heap[x].reserve((size_t)(G / kNumXcds + 1));
     for (int w = 0; w < G; ++w) heap[w % kNumXcds].push_back(Slot(0, w));
     auto later = [](const Slot& a, const Slot& b) { return a > b; };
     for (uint32_t i : order) {
