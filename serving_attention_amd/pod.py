@@ -195,7 +195,8 @@ class BatchPOD:
         self.kv_layout = kv_layout
         self.device = float_workspace_buffer.device
         self._float_ws = float_workspace_buffer
-        self._int_ws = torch.zeros(int_workspace_bytes // 4, dtype=torch.int32, device=self.device)
+        # every plan copies a whole image (its counters zeroed) into the half it uses
+        self._int_ws = torch.empty(int_workspace_bytes // 4, dtype=torch.int32, device=self.device)
         ctx = ctypes.c_void_p()
         dev = self.device.index if self.device.index is not None else 0
         fws = (ctypes.c_void_p(self._float_ws.data_ptr()), self._float_ws.numel() * self._float_ws.element_size())

@@ -362,10 +362,10 @@ def test_group_128(dtype):
 
 def test_first_plan_waits_for_work_queued_on_the_stream():
     """A new context planned right behind a few milliseconds of queued work on
-    the caller's stream (which also zero-fills the new int workspace): the
-    first image copy of each workspace half is ordered after that work, so the
-    launch reads the plan and not a workspace cleared after the copy. Outputs
-    start as NaN, so a launch that found no work would show."""
+    the caller's stream: the first image copy of each workspace half is
+    ordered after that work (a caller may still be initialising or using that
+    memory there), so the launch reads the plan. Outputs start as NaN, so a
+    launch that found no work would show."""
     log("case: first plans behind queued work on the stream")
     w = build(small_spec(p_q=(70,), p_kv=(300,), d_kv=(1, 700, 2049), dq=2), device="cuda")
     ref = None
@@ -391,3 +391,48 @@ def test_first_plan_waits_for_work_queued_on_the_stream():
             for a, b in zip(ref, outs + lses):
                 assert torch.equal(a, b), f"trial {trial} plan {rep}: outputs differ"
         del pod
+
+
+def test_plan_and_run_on_other_streams():
+    """Plans on one stream and runs on another, alternating plans made while
+    the previous launch is still queued (the host then waits for the work-list
+    copy) with plans made on an idle GPU (the launch then waits for the copy on
+    the device): every run reads its own plan. Two workloads alternate, so a
+    launch that read the other plan's list would not match."""
+    log("case: plans and runs on different streams, GPU busy and idle")
+    wls = [build(small_spec(p_q=(70,), p_kv=(300,), d_kv=(1, 700, 2049), dq=2), device="cuda"),
+           build(small_spec(p_q=(33, 5), p_kv=(33, 400), d_kv=(900, 17), dq=1, seed=7), device="cuda")]
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    pod = BatchPOD(ws, "NHD", int_workspace_bytes=4 << 20)
+    busy = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    s_plan, s_run = torch.cuda.Stream(), torch.cuda.Stream()
+    kept = []
+    for it in range(8):
+        w = wls[it % 2]
+        p, d = w.prefill, w.decode
+        idle = it % 4 >= 2
+        if idle:
+            torch.cuda.synchronize()
+        with torch.cuda.stream(s_plan):
+            pod.plan(p.qo_indptr, p.kv_indptr, p.last_page_len, d.qo_indptr, d.kv_indptr,
+                     d.last_page_len, num_qo_heads=16, num_kv_heads=4, head_dim=128, page_size=16,
+                     dtype=torch.bfloat16, decode_chunk=256)
+        outs = [torch.full_like(r.q, float("nan")) for r in (p, d)]
+        lses = [torch.full(r.q.shape[:2], float("nan"), device="cuda") for r in (p, d)]
+        s_run.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s_run):
+            if not idle:
+                busy.fill_(float(it))         # the launch queues behind ~1 GB of writes
+            res = pod.run(p.q, p.kv_cache, p.kv_indices_dev, d.q, d.kv_cache, d.kv_indices_dev,
+                          return_lse=True, out_p=outs[0], lse_p=lses[0], out_d=outs[1], lse_d=lses[1])
+        kept.append((it % 2, res, outs + lses))
+    torch.cuda.synchronize()
+    first = {}
+    for it, (k, res, ts) in enumerate(kept):
+        if k not in first:
+            check_all(wls[k], res, f"streams-{k}")
+            first[k] = ts
+            continue
+        for a, b in zip(first[k], ts):
+            assert torch.equal(a, b), f"iteration {it}: outputs differ from the first run of this plan"
