@@ -47,6 +47,7 @@ CASES = [
     dict(hqo=64, hkv=1, dq=1),                              # group 64: two slices
     dict(hqo=16, hkv=2, dq=5, w=300, sinks=True),           # 8 x 5 = 40 rows: 32 + 8
     dict(hqo=128, hkv=2, dq=2, ps=1, scales=(0.5, 2.0, 1.5)),  # 64 x 2 = 128 rows: four slices
+    dict(hqo=64, hkv=2, dq=1, layout="HND", w=100, sinks=True, p_q=()),  # slices over HND pools
 ]
 
 
