@@ -74,6 +74,34 @@ def kv_views(cache: KVCache, kv_layout: str):
     raise ValueError(f"unknown kv_layout {kv_layout!r}")
 
 
+def _kv_geometry(cache: KVCache, kv_layout: str):
+    """What a launch needs of a paged cache, read from the tensor metadata
+    without building views: (k address, v address, dtype, device, pages,
+    page_size, kv heads, head_dim, page / token / head strides in elements).
+    The same checks as kv_views."""
+    if isinstance(cache, (tuple, list)):
+        k, v = cache
+        if k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride():
+            raise ValueError("k and v caches must be 4-D with equal shapes and strides")
+        shape, st = k.shape, k.stride()
+        kp, vp, dt, dev = k.data_ptr(), v.data_ptr(), k.dtype, k.device
+    else:
+        if cache.dim() != 5 or cache.shape[1] != 2:
+            raise ValueError("combined paged cache must be [pages, 2, ...]")
+        cs = cache.stride()
+        shape = (cache.shape[0],) + tuple(cache.shape[2:])
+        st = (cs[0],) + tuple(cs[2:])
+        kp, dt, dev = cache.data_ptr(), cache.dtype, cache.device
+        vp = kp + cs[1] * cache.element_size()
+    if st[3] != 1:
+        raise ValueError("head_dim must be the innermost, dense dimension")
+    if kv_layout == "NHD":
+        return kp, vp, dt, dev, shape[0], shape[1], shape[2], shape[3], st[0], st[1], st[2]
+    if kv_layout == "HND":
+        return kp, vp, dt, dev, shape[0], shape[2], shape[1], shape[3], st[0], st[2], st[1]
+    raise ValueError(f"unknown kv_layout {kv_layout!r}")
+
+
 def _plan_record(keep, present, num_qo_heads, num_kv_heads, head_dim, page_size, dtype, sinks,
                  kv_dtype_d) -> dict:
     """What run() checks its tensors against. keep holds (qo, kv, lpl) of each
@@ -107,22 +135,22 @@ def _role_args(pl, kv_layout, graph, idx, q, cache, kv_indices, out, lse):
         raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, "q dtype differs from the planned dtype")
     if q.stride(-1) != 1:
         raise ValueError("q: head_dim must be dense")
-    k, v, sp, st, sh = kv_views(cache, kv_layout)
+    kp, vp, kdt, kdev, pages, ps, hk, kd, sp, st, sh = _kv_geometry(cache, kv_layout)
     want = torch.float8_e4m3fn if (idx == 1 and pl["fp8_d"]) else q.dtype
-    if k.dtype != want:
-        raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, f"kv dtype {k.dtype} differs from the planned {want}")
-    ps = k.shape[1] if kv_layout == "NHD" else k.shape[2]
-    hk = k.shape[2] if kv_layout == "NHD" else k.shape[1]
-    if ps != pl["page_size"] or hk != pl["num_kv_heads"] or k.shape[3] != d:
+    if kdt != want:
+        raise _lib.PodError(_lib.POD_ERR_NOT_PLANNED, f"kv dtype {kdt} differs from the planned {want}")
+    if ps != pl["page_size"] or hk != pl["num_kv_heads"] or kd != d:
         raise ValueError("paged cache shape differs from the plan")
+    if kdev != q.device:
+        raise ValueError("the paged cache must be on q's device")
     nnz = pl["nnz"][idx]
     if kv_indices is not None:
         if kv_indices.dtype != torch.int32 or not kv_indices.is_cuda or kv_indices.dim() != 1:
             raise ValueError("kv_indices must be a 1-D int32 device tensor")
         if kv_indices.numel() < nnz:
             raise ValueError(f"kv_indices holds {kv_indices.numel()} pages, the plan needs {nnz}")
-    elif k.shape[0] < nnz:
-        raise ValueError(f"identity page table needs {nnz} pages, the cache has {k.shape[0]}")
+    elif pages < nnz:
+        raise ValueError(f"identity page table needs {nnz} pages, the cache has {pages}")
     # outputs: the kernel writes 16-byte vectors of a dense head_dim and the
     # LSE at row * num_qo_heads + head
     if not isinstance(out, torch.Tensor) or out.dim() != 3 or out.shape[0] < q.shape[0] \
@@ -136,7 +164,7 @@ def _role_args(pl, kv_layout, graph, idx, q, cache, kv_indices, out, lse):
         if lse.dtype != torch.float32 or lse.device != q.device or lse.stride() != (hq, 1):
             raise ValueError("lse must be a contiguous float32 tensor on q's device")
     return _lib.PodRoleArgs(
-        q.data_ptr(), q.stride(0), q.stride(1), k.data_ptr(), v.data_ptr(), sp, st, sh,
+        q.data_ptr(), q.stride(0), q.stride(1), kp, vp, sp, st, sh,
         kv_indices.data_ptr() if kv_indices is not None else None,
         out.data_ptr(), out.stride(0), out.stride(1),
         lse.data_ptr() if lse is not None else None)

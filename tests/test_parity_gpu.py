@@ -265,6 +265,14 @@ def test_run_errors():
     for kw in bad_outs:
         with pytest.raises(ValueError):
             pod.run(*args, **kw)
+    # the paged caches: on q's device, of the planned dtype and shape (combined
+    # [P, 2, ...] cache or a (k, v) pair)
+    kc = w.decode.kv_cache
+    bad_caches = [kc.cpu(), kc.half(), kc[:, :, :8], (kc[:, 0], kc[:, 1, :, :1]), kc[:, :1]]
+    for c in bad_caches:
+        with pytest.raises((ValueError, _lib.PodError)):
+            pod.run(w.prefill.q, w.prefill.kv_cache, w.prefill.kv_indices_dev,
+                    w.decode.q, c, w.decode.kv_indices_dev)
     # the decode scales: finite, q_scale * k_scale > 0, effective scale <= 1e6
     for kw in (dict(q_scale_d=-1.0), dict(k_scale_d=float("nan")), dict(v_scale_d=float("inf")),
                dict(q_scale_d=1e4, k_scale_d=1e4)):
