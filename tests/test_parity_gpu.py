@@ -70,6 +70,11 @@ GRID = [
     dict(dtype="bf16", ps=16, hqo=64, hkv=1, dq=2),      # group 64: decode runs as query tiles
     dict(dtype="bf16", ps=16, hqo=12, hkv=4, w=0),       # group 3, diagonal-only window
     dict(dtype="bf16", ps=16, hqo=16, hkv=4, layout="HND"),
+    # limits: the most sink heads the query tiles stage (1024 query heads, group 128)
+    dict(dtype="bf16", ps=16, hqo=1024, hkv=8, sinks=True, dq=1, p_q=(40, 3), p_kv=(40, 300),
+         d_kv=(1, 300, 1100)),
+    dict(dtype="bf16", ps=64, hqo=16, hkv=4, w=200, sinks=True, dq=2),   # large power-of-two pages
+    dict(dtype="f16", ps=48, hqo=16, hkv=4, dq=3),                       # large other pages
 ]
 
 
@@ -349,6 +354,23 @@ def test_non_causal_roles(w, dq, hqo):
     wl = build(spec, device="cuda")
     res, _ = plan_and_run(wl)
     check_all(wl, res, f"noncausal-w{w}-q{dq}")
+
+
+@pytest.mark.parametrize("w", [-1, 10])
+def test_non_causal_more_queries_than_keys(w):
+    """Non-causal requests may hold more query rows than keys: the diagonal
+    kv_len - q_len + i is negative for the first rows, every row sees all keys
+    (up to its window's left bound, which then lies before key 0)."""
+    log(f"case: non-causal, q_len > kv_len (window_left={w})")
+    spec = WorkloadSpec(
+        name="noncausal_short_kv",
+        prefill=RoleSpec([200, 70, 33], [50, 20, 1], causal=False, window_left=w),
+        decode=RoleSpec([5, 5, 3], [3, 40, 1], causal=False, window_left=w),
+        num_qo_heads=16, num_kv_heads=4, page_size=16, dtype="bf16", sinks=True, pool="shared",
+        shuffle_pages=True, spare_pages=3, meta_seed=312, value_seed=412)
+    wl = build(spec, device="cuda")
+    res, _ = plan_and_run(wl)
+    check_all(wl, res, f"noncausal-short-w{w}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
