@@ -423,3 +423,63 @@ def test_bf16_large_group_decode_still_uses_tiles():
     rc, img, info = compute(desc)
     im = decode_image(img)
     assert not any(int(it[0]) & FLAG_CHUNK for it in im["items"])
+
+
+# ------------------------------------------------------------ random plans (property test)
+
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+
+@st.composite
+def random_plans(draw):
+    hkv = draw(st.sampled_from([1, 2, 4, 8]))
+    g = draw(st.sampled_from([1, 2, 3, 8, 16, 64, 128]))
+    ps = draw(st.sampled_from([1, 5, 16, 64]))
+    fp8 = draw(st.booleans())
+    roles = []
+    for role in ("prefill", "decode"):
+        n = draw(st.integers(0, 4))
+        if n == 0:
+            roles.append(None)
+            continue
+        causal = draw(st.booleans())
+        w = draw(st.sampled_from([-1, 0, 7, 100]))
+        max_q = 90 if role == "prefill" else 6
+        q_lens = draw(st.lists(st.integers(0 if role == "prefill" else 1, max_q), min_size=n, max_size=n))
+        kv_lens = [draw(st.integers(max(1, q if causal else 1), 400)) for q in q_lens]
+        roles.append(dict(qo_lens=q_lens, kv_lens=kv_lens, causal=causal, window_left=w))
+    return dict(hkv=hkv, g=g, ps=ps, fp8=fp8, roles=roles,
+                chunk=draw(st.sampled_from([0, 64, 192, -1])), order=draw(st.integers(0, 3)),
+                num_cus=draw(st.sampled_from([4, 8, 40, 256])))
+
+
+@settings(max_examples=60, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(random_plans())
+def test_random_plans_cover_every_visible_key_once(plan):
+    """Random plans of both roles: every (row, kv head, visible key) is covered
+    exactly once, split groups are consistent, every item sits in one
+    workgroup list or in the shared pool, a grid below the CU count gives each
+    workgroup at most one item and no pool, and an FP8 decode cache puts every
+    decode item in a key chunk."""
+    hkv, g = plan["hkv"], plan["g"]
+    if g * hkv > 1024:
+        g = max(1, 1024 // hkv)
+    roles = plan["roles"]
+    desc, keep = plan_desc(prefill=roles[0], decode=roles[1], hqo=hkv * g, hkv=hkv, page_size=plan["ps"],
+                           num_cus=plan["num_cus"], decode_chunk=plan["chunk"], order=plan["order"])
+    if plan["fp8"]:
+        desc.decode_kv_dtype = _lib.POD_DTYPE_FP8_E4M3
+    rc, img, info = compute(desc)
+    assert rc == _lib.POD_OK
+    spec = [(r["qo_lens"], r["kv_lens"], r["causal"], r["window_left"]) if r else ([], [], True, -1)
+            for r in roles]
+    im = check_coverage(img, spec, hkv * g, hkv)
+    grid = info.grid
+    assert 0 < grid <= plan["num_cus"]
+    pf, pc = im["pool_first"], im["pool_count"]
+    assert np.all(im["wg_of_item"][:pf] >= 0) and np.all(im["wg_of_item"][pf:] == -1)
+    assert all(int(it[0]) & FLAG_CHUNK for it in im["items"][pf:])
+    if grid < plan["num_cus"]:
+        assert pc == 0 and all(int(wg[1]) + int(wg[2]) <= 1 for wg in im["wgs"])
+    if plan["fp8"]:
+        assert all(int(it[0]) & FLAG_CHUNK for it in im["items"] if int(it[0]) & FLAG_ROLE)
