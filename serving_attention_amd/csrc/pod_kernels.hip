@@ -445,7 +445,7 @@ __device__ __forceinline__ TileDesc tile_desc(CI32* tdesc, int idx) {
 }
 
 
-template <typename T, bool kPow2>
+template <typename T, bool kPow2, int kPaged>
 __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd, int t0, int nt, const int32_t* tab,
                             int nv, char* ring, char* idring, float* sink_lds, char* pf_lds) {
   using V8 = typename Dt<T>::v8;
@@ -463,7 +463,10 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
   const RoleView r = pick_role(p, role, 0);
   const char* const kpool = r.k;
   const char* const vpool = r.v;
-  const bool paged = r.indices != nullptr;
+  // kPaged: 1 the role has a page table, 0 identity pages, 2 read here (the
+  // power-of-two page sizes, which every serving workload uses, get the first
+  // two as separate code: no select between the two page sources per load)
+  const bool paged = kPaged == 2 ? r.indices != nullptr : kPaged == 1;
   // page-id loads read the page table, or word 0 of the request table (unused)
   const int32_t* const id_src = paged ? r.indices : image_region(p, kHdrReqs);
   const uint32_t kv_sp = r.kv_sp_b, kv_st = r.kv_st_b;
@@ -1568,10 +1571,13 @@ __global__ __launch_bounds__(kThreads, 1) void pod_grid_kernel(Params) {
       if (nb == 0) continue;
       if (role && pre_blk) __syncthreads();
       const int t0 = role ? pre_tiles : 0, nt = role ? n_tiles - pre_tiles : pre_tiles;
-      if (p.page_shift >= 0)
-        tile_stream<T, true>(p, role, ttd, t0, nt, tb + (int64_t)b0 * kBlockWords, nb, lds, ids, sink_lds, pf_lds);
+      const int32_t* tbr = tb + (int64_t)b0 * kBlockWords;
+      if (p.page_shift >= 0 && p.role[role].indices != nullptr)
+        tile_stream<T, true, 1>(p, role, ttd, t0, nt, tbr, nb, lds, ids, sink_lds, pf_lds);
+      else if (p.page_shift >= 0)
+        tile_stream<T, true, 0>(p, role, ttd, t0, nt, tbr, nb, lds, ids, sink_lds, pf_lds);
       else
-        tile_stream<T, false>(p, role, ttd, t0, nt, tb + (int64_t)b0 * kBlockWords, nb, lds, ids, sink_lds, pf_lds);
+        tile_stream<T, false, 2>(p, role, ttd, t0, nt, tbr, nb, lds, ids, sink_lds, pf_lds);
     }
   }
   if (!chunks_first) run_chunks();

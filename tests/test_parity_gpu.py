@@ -466,3 +466,30 @@ def test_plan_and_run_on_other_streams():
             continue
         for a, b in zip(first[k], ts):
             assert torch.equal(a, b), f"iteration {it}: outputs differ from the first run of this plan"
+
+
+@pytest.mark.parametrize("ps", [16, 5])
+def test_identity_pages_for_query_tiles(ps):
+    """Roles run without a page table (identity pages: page i of a request's
+    range is pool page i): the query tiles' own code for identity pages
+    (power-of-two page sizes) and the code that decides it per launch (other
+    page sizes), for the prefill role and for decode rows that run as query
+    tiles (group 16 x q_len 3 = 48 rows)."""
+    log(f"case: identity pages through query tiles (page_size={ps})")
+    spec = WorkloadSpec(
+        name="identity_tiles", prefill=RoleSpec([70, 1, 130], [200, 1, 130], causal=True, window_left=-1),
+        decode=RoleSpec([3, 1, 3], [3, 90, 700], causal=True, window_left=40),
+        num_qo_heads=32, num_kv_heads=2, page_size=ps, dtype="bf16", sinks=True, pool="separate",
+        shuffle_pages=False, spare_pages=0, meta_seed=321, value_seed=421)
+    w = build(spec, device="cuda")
+    for r in (w.prefill, w.decode):
+        assert np.array_equal(r.kv_indices, np.arange(len(r.kv_indices)))
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    pod = BatchPOD(ws, "NHD", int_workspace_bytes=4 << 20)
+    p, d = w.prefill, w.decode
+    pod.plan(p.qo_indptr, p.kv_indptr, p.last_page_len, d.qo_indptr, d.kv_indptr, d.last_page_len,
+             num_qo_heads=32, num_kv_heads=2, head_dim=128, page_size=ps, dtype=torch.bfloat16,
+             window_left_d=40, sinks=True)
+    res = pod.run(p.q, p.kv_cache, None, d.q, d.kv_cache, None, sinks=w.sinks, return_lse=True)
+    torch.cuda.synchronize()
+    check_all(w, res, f"identity-tiles-ps{ps}")
