@@ -402,7 +402,10 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
     e = hipMemcpyAsync(ctx->int_ws, ctx->staging[k], bytes, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (work list)");
     e = hipEventRecord(ctx->staged[k], s);   // the staging buffer is free again after it
-    if (e != hipSuccess) return hip_err(e, "hipEventRecord");
+    if (e != hipSuccess) {
+      (void)hipStreamSynchronize(s);   // the copy still reads the staging buffer
+      return hip_err(e, "hipEventRecord");
+    }
     ctx->staged_pending[k] = true;
     ctx->next_staging = 1 - k;
     if (!ctx->policy_set) {
@@ -434,7 +437,11 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
   e = hipMemcpyAsync(int_half(ctx, k), ctx->staging[k], bytes, hipMemcpyHostToDevice, ctx->copy_stream);
   if (e != hipSuccess) return hip_err(e, "hipMemcpyAsync (work list)");
   e = hipEventRecord(ctx->staged[k], ctx->copy_stream);
-  if (e != hipSuccess) return hip_err(e, "hipEventRecord");
+  if (e != hipSuccess) {
+    (void)hipStreamSynchronize(ctx->copy_stream);   // the copy still reads the staging buffer
+    return hip_err(e, "hipEventRecord");
+  }
+  ctx->staged_pending[k] = true;   // the staging buffer is read until the copy ends
   // While the previous plan's launch still runs, the host waits for this copy
   // behind it (a few microseconds; the launch keeps the GPU busy), so pod_run
   // enqueues the next launch alone: a cross-stream wait ahead of each launch
@@ -456,8 +463,6 @@ int pod_plan(pod_ctx_t ctx, const pod_plan_desc* desc, void* stream) {
     e = hipEventSynchronize(ctx->staged[k]);
     if (e != hipSuccess) return hip_err(e, "hipEventSynchronize");
     ctx->staged_pending[k] = false;
-  } else {
-    ctx->staged_pending[k] = true;
   }
   ctx->cur = k;
   ctx->next_staging = 1 - k;
