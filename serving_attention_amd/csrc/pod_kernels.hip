@@ -794,10 +794,13 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
   // Block v streams into ring slot v % 4 and its page ids into id slot v % 4.
   // Iteration t reads slots t-1 and t and issues the K/V loads of block t+2
   // (4 loads, into the slot of block t-2) and then the ids of block t+6 (1
-  // load), and moves the ids of block t+3 to registers; waves 0-3 issue all of
-  // it around their M turn, so their softmax turn holds no load work. The
-  // prologue issues what iterations -2 and -1 would have, after the sinks (LDS
-  // copy, for the tiles' final normalisation) and the first tile's query.
+  // load), and moves the ids of block t+3 to registers. Waves 0-3 issue all of
+  // it at the start of their softmax turn, so their MFMA turn holds no load
+  // work (a wave that mixes other instructions into its MFMA stream issues the
+  // MFMAs more slowly); waves 4-7 issue theirs around their MFMA turn, which
+  // keeps their loads a turn further ahead. The prologue issues what
+  // iterations -2 and -1 would have, after the sinks (LDS copy, for the tiles'
+  // final normalisation) and the first tile's query.
   setup(cur);
   load_query(cur);
   // Pull the block table and the tiles' boundary rows into L2 (one word per
@@ -840,8 +843,9 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
   };
   // Item boundaries: block t opens a new item (first block): after the M turn
   // that ends the previous item's P.V, that item is normalised and stored and
-  // the new one's state reset (placed so that the stores never sit between a
-  // block's loads and the wait for them). Block t closes its item (the next
+  // the new one's state reset (the stores follow the loads of block t+2 and
+  // make the wait for that block count them too, which only delays it until
+  // they have drained). Block t closes its item (the next
   // block opens one): after the M turn of S_t the next item's query goes to the
   // registers and is waited for at once (with every load issued before it):
   // one load latency per item, and no wait on the query in the other passes.
@@ -851,9 +855,9 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
     Ent e2 = ent(2), e6 = ent(6);
     {
       top(0);
-      dma_rows(2, 0, e2);
       m_s(0);
       ring_barrier();
+      dma_rows(2, 0, e2);
       dma_rows(2, 1, e2);
       load_ids(6, e6);
       read_ids(3);
@@ -872,12 +876,12 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
       const bool bnd = is_first(ea);
       const bool nq = t + 1 < nv && is_first(eb);
       top(t);
-      dma_rows(t + 2, 0, e2);
       m_both(t);
+      ring_barrier();
+      dma_rows(t + 2, 0, e2);
       dma_rows(t + 2, 1, e2);
       load_ids(t + 6, e6);
       read_ids(t + 3);
-      ring_barrier();
       if (bnd) {
         finish(cur);
         cur = item_idx(ea);
@@ -898,9 +902,9 @@ __device__ __forceinline__ void tile_stream(PArg p, int role, const int32_t* ttd
     }
     {
       top(nv);
-      dma_rows(nv + 2, 0, e2);
       m_pv(nv - 1);
       ring_barrier();
+      dma_rows(nv + 2, 0, e2);
       dma_rows(nv + 2, 1, e2);
       load_ids(nv + 6, e6);
       read_ids(nv + 3);
