@@ -199,6 +199,7 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
   }
   std::vector<Item> items(n_items_total);
   std::vector<int32_t> groups;  // n_groups x 4
+  groups.reserve(n_items_total * kGroupWords);
   int32_t n_slots = 0;
   size_t ni = 0;
   for (size_t ri = 0; ri < reqs.size(); ++ri) {
@@ -347,12 +348,11 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
   // and the grid need not stay fixed, as many per die as the most items a die
   // holds, so a small step launches few idle workgroups.
   int G = num_cus;
-  if (!fixed_grid) {
-    int64_t per_die[kNumXcds] = {};
-    for (const Item& it : items) ++per_die[it.xcd];
-    const int64_t most = std::max<int64_t>(1, *std::max_element(per_die, per_die + kNumXcds));
-    if (most * kNumXcds < num_cus) G = (int)(most * kNumXcds);
-  }
+  int64_t per_die[kNumXcds] = {};
+  for (const Item& it : items) ++per_die[it.xcd];
+  const int64_t most = std::max<int64_t>(1, *std::max_element(per_die, per_die + kNumXcds));
+  const bool one_each = most * kNumXcds <= num_cus;
+  if (!fixed_grid && one_each) G = (int)(most * kNumXcds);
   // The shared pool: the lightest key chunks, up to kPoolShare of their cost
   // (none when every item has a workgroup of its own).
   const bool use_pool = G > 1 && items.size() > (size_t)G;
@@ -380,7 +380,7 @@ int plan_compute(const pod_plan_desc& d, const ImageSink& sink, pod_plan_info& i
   // of its workgroups (LPT), so every workgroup holds a static list.
   // Per die a min-heap of (load, workgroup); ties go to the lower workgroup.
   std::vector<int32_t> wg_of(items.size(), -1);
-  if (G < num_cus) {
+  if (one_each) {
     // every die's items fit one workgroup each: the heap below would hand die
     // x's items, in order, to its workgroups x, x + 8, ... (all still empty)
     int32_t next[kNumXcds];
