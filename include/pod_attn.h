@@ -201,9 +201,10 @@ typedef struct pod_plan_info {
   int32_t n_decode_items;
   int32_t n_groups;         /* split (request, kv head) units that need the LSE merge */
   int32_t n_slots;          /* partial-state slots in the float workspace */
-  int32_t grid;             /* persistent workgroups launched: one per CU, or, for a
-                               plan with fewer items than CUs (outside graph mode),
-                               one per item rounded up to a multiple of 8 */
+  int32_t grid;             /* persistent workgroups launched: one per CU, or, when
+                               no die holds more items than it has CUs (outside
+                               graph mode), 8 x the most items any die holds, each
+                               workgroup then running one item */
   int32_t decode_chunk;     /* keys per decode split actually used */
   int32_t image_ints;       /* int32 words of the work-list image */
   int64_t float_ws_bytes;   /* float workspace the plan needs */
