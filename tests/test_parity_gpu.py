@@ -136,6 +136,43 @@ def test_many_chunks_per_workgroup(idx):
     check_all(w, res, f"many{idx}")
 
 
+TILES = [
+    dict(dtype="bf16", ps=16, w=-1, sinks=True, hqo=16, hkv=8),
+    dict(dtype="f16", ps=16, w=40, sinks=False, hqo=32, hkv=4),
+    dict(dtype="bf16", ps=5, w=-1, sinks=True, hqo=16, hkv=8),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(TILES)), ids=[str(i) for i in range(len(TILES))])
+def test_many_query_tiles_per_workgroup(idx):
+    """Hundreds of short prefill requests (chunks on prefixes, 1-150 rows) and a
+    decode batch whose q_len x group exceeds 32 rows, so both roles run as query
+    tiles: each workgroup streams several tiles per role with an item boundary
+    every one to a few key blocks (normalise and store, reset, next query), and
+    the loads of later blocks are in flight across those boundaries."""
+    cfg = TILES[idx]
+    rng = np.random.default_rng(70 + idx)
+    n_p, n_d = 400, 60
+    pq = rng.integers(1, 151, n_p).tolist()
+    pkv = [int(q + x) for q, x in zip(pq, rng.integers(0, 200, n_p))]
+    g = cfg["hqo"] // cfg["hkv"]
+    dq = rng.integers(32 // g + 1, 32 // g + 9, n_d).tolist()
+    dkv = [int(q + x) for q, x in zip(dq, rng.integers(0, 400, n_d))]
+    spec = WorkloadSpec(
+        name="many_tiles", prefill=RoleSpec(pq, pkv, causal=True, window_left=cfg["w"]),
+        decode=RoleSpec(dq, dkv, causal=True, window_left=cfg["w"]),
+        num_qo_heads=cfg["hqo"], num_kv_heads=cfg["hkv"], page_size=cfg["ps"], dtype=cfg["dtype"],
+        sinks=cfg["sinks"], pool="shared", shuffle_pages=True, spare_pages=2, meta_seed=500 + idx,
+        value_seed=600 + idx)
+    log(f"case: many query tiles per workgroup {idx} {cfg}")
+    w = build(spec, device="cuda")
+    res, pod = plan_and_run(w)
+    info = pod.plan_info()
+    log(f"plan: {info}")
+    assert info["n_prefill_items"] > 2 * info["grid"]
+    check_all(w, res, f"tiles{idx}")
+
+
 def test_repeat_runs_are_bitwise_stable_and_counters_reset():
     log("case: repeated runs with split-KV")
     w = build(small_spec(dq=2, sinks=True), device="cuda")
