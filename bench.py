@@ -78,11 +78,37 @@ def work_counts(w):
     return out
 
 
+def _code_only(text):
+    """C/C++ source without comments and blank space (string literals kept), so
+    an edit of a comment does not mark the measured kernel as changed."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash():
+    """Hash of the code (comments and spacing left out) of the sources that
+    decide what the kernel reads and writes."""
     h = hashlib.sha256()
     for f in ("planner.cpp", "pod_api.cpp", "pod_kernels.hip", "pod_internal.h"):
-        with open(os.path.join(ROOT, "serving_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "serving_attention_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

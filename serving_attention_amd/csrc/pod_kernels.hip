@@ -25,12 +25,16 @@
 // the row index swapped, so each lane half's score accumulators cover 8
 // consecutive keys and the P^T operand comes straight from them.
 //
-// LDS layout: K and V blocks are row-major, one 256-byte row per key (one kv
-// head's 128 dims), with the 16-byte chunks of row `key` permuted by
-// XOR with swz(key). Sixteen consecutive keys then put any fixed chunk in 16
-// distinct bank groups (conflict-free row writes and K operand reads), and the
-// 4-key x 16-dim blocks read by ds_read_b64_tr_b16 for the V^T operand fall in
-// disjoint banks for the two 16-lane groups of each half wave.
+// LDS layout: one 256-byte row per key (one kv head's 128 dims). Key chunks
+// (a block per wave, rows written from registers) permute the 16-byte chunks
+// of row `key` by XOR with swz(key): sixteen consecutive keys then put any
+// fixed chunk in 16 distinct bank groups (conflict-free row writes and K
+// operand reads), and the 4-key x 16-dim blocks read by ds_read_b64_tr_b16 for
+// the V^T operand fall in disjoint banks for the two 16-lane groups of each
+// half wave. Query-tile ring slots keep the rows as the direct-to-LDS loads
+// write them (four 256-byte rows per load instruction) and place row R at
+// (R % 16) * group stride + (R / 16) * 256, with the group stride padded (1040
+// bytes for K, 1088 for V) for the same bank spread.
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 

@@ -85,3 +85,12 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
+
+
+def test_source_hash_ignores_comments_only():
+    code = 'int f(int x) {\n  // one\n  return x + 1; /* two */\n}\nconst char* s = "a // b /* c */";\n'
+    same = 'int f(int x) {\n  // another comment\n\n  return x + 1;   /* changed */\n}\nconst char* s = "a // b /* c */";\n'
+    other = 'int f(int x) {\n  return x + 2;\n}\nconst char* s = "a // b /* c */";\n'
+    assert bench._code_only(code) == bench._code_only(same)
+    assert bench._code_only(code) != bench._code_only(other)
+    assert '"a // b /* c */"' in bench._code_only(code)
